@@ -1,0 +1,212 @@
+/*
+ * vts.h -- exact batched variable-length top-K selection (C ABI).
+ *
+ * Two operations, both asynchronous on the caller's HIP stream, both exact
+ * with ties interchangeable:
+ *
+ *   vts_topk_varlen                 decode-step top-k with per-request lengths
+ *   vts_topk_page_table_transform   top-k over row windows, fused with a
+ *                                   page-table translation of the indices
+ *
+ * The unprefixed names topk_varlen and topk_page_table_transform are exported
+ * as aliases of the two entry points.
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked "device" are HIP device memory (or memory the device can
+ *     read/write directly); the caller owns all of it.  The library allocates
+ *     nothing during a call and reads no device memory from the host, so a call
+ *     may be captured into a HIP graph.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  The
+ *     call only enqueues work; results are ready when the stream reaches it.
+ *   - Integers in device arrays (lengths, starts, hints) may hold any value: the
+ *     kernels clamp them as described and never read out of bounds because of
+ *     them.
+ *   - Return value: a vts_status.  Argument errors are detected on the host
+ *     before any HIP call, so nothing is enqueued when a call fails.
+ */
+#ifndef VTS_H
+#define VTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of the score rows. */
+typedef enum { VTS_F32 = 0, VTS_BF16 = 1, VTS_F16 = 2 } vts_dtype;
+
+typedef enum {
+    VTS_OK = 0,
+    /* pre_idx was not usable (misaligned); it was ignored and the call ran
+     * without a hint.  Results are unaffected.  (FlashInfer top_k_varlen doc,
+     * `pre_idx`: a malformed hint is discarded with a warning.) */
+    VTS_WARN_HINT_DISCARDED = 1,
+    /* a shape, pointer, alignment or grouping argument breaks the contract
+     * (FlashInfer top_k_varlen doc, "raises ValueError"). */
+    VTS_ERR_INVALID = -1,
+    /* the request is valid but outside what this library implements:
+     * top_k outside [1, 2048], width above 2^31 - 1, or a device other than
+     * gfx950. */
+    VTS_ERR_UNSUPPORTED = -2,
+    /* workspace pointer null or smaller than the matching *_workspace_bytes(). */
+    VTS_ERR_WORKSPACE = -3,
+    /* a HIP runtime call failed (no device, launch failure). */
+    VTS_ERR_HIP = -4
+} vts_status;
+
+/* Workspace: device scratch used by rows that several workgroups share and by
+ * candidate overflow.  Query its size with the matching *_workspace_bytes()
+ * (a pure host function of the shape), allocate it, fill it with zeros ONCE
+ * (vts_workspace_init or any memset), then pass it to every call of that
+ * shape.  Each call leaves it as it found it apart from the event counters of
+ * vts_workspace_stats, so it never needs clearing again.  One workspace must
+ * not be used by two calls that can run at the same time (for example on two
+ * streams): give each stream its own.  (FlashInfer top_k_varlen doc,
+ * `workspace`: a zero-initialised, self-restoring slab, one per stream.) */
+size_t vts_topk_varlen_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k,
+                                       int32_t dtype);
+size_t vts_page_transform_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k,
+                                          int32_t dtype);
+
+/* Fills `bytes` bytes of `workspace` with zeros on `stream`. */
+int vts_workspace_init(void* workspace, size_t bytes, void* stream);
+
+/*
+ * vts_topk_varlen -- FlashInfer "flashinfer.top_k_varlen" documentation
+ * (signature, `seq_lens`, `compress_ratio`, `next_n`, `pre_idx`,
+ * `return_values`, `out_indices`, `out_values`).
+ *
+ * logits      device, dtype elements, num_rows rows of `width` columns with
+ *             consecutive rows `row_stride` elements apart (row_stride >=
+ *             width); the base must be aligned to the element size.
+ * seq_lens    device int32[num_rows / next_n]: KV-cache length of each request
+ *             in KV-token units.  Row r belongs to request i = r / next_n as its
+ *             t = r % next_n-th row and ranks its first
+ *               n = max(0, (seq_lens[i] - next_n + t + 1) / compress_ratio)
+ *             columns (integer division), clamped to `width`.
+ * top_k       1 <= top_k <= 2048.
+ * next_n      >= 1, must divide num_rows.
+ * compress_ratio >= 1.
+ * pre_idx     device int32[num_rows / next_n, top_k] or NULL: the previous
+ *             step's selection for each request, used only to steer the
+ *             threshold estimate (entries outside [0, n) are ignored).  Must be
+ *             16-byte aligned; otherwise it is ignored and the call returns
+ *             VTS_WARN_HINT_DISCARDED.  Results never depend on it.
+ * out_indices device int32[num_rows, top_k], 16-byte aligned.  Row r receives
+ *             the column indices of its top-k (in no particular order) when
+ *             n > top_k; the indices 0..n-1 followed by -1 when n <= top_k (all
+ *             -1 when n == 0).
+ * out_values  device dtype[num_rows, top_k], 16-byte aligned, or NULL (values
+ *             not returned).  Bit copies of the selected elements, aligned
+ *             with out_indices; slots holding -1 get the lowest finite value
+ *             of the dtype (-FLT_MAX for fp32, 0xFF7F bf16, 0xFBFF fp16).
+ * workspace   device, >= vts_topk_varlen_workspace_bytes(num_rows, width,
+ *             top_k, dtype) bytes, 16-byte aligned, zeroed once (see above).
+ *
+ * Ties: all elements that compare equal are interchangeable; -0 and +0 are
+ * ties.  +inf, -inf and subnormals rank exactly.  NaN is ordered above +inf
+ * (sign clear) or below -inf (sign set).
+ */
+int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                    int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
+                    int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
+                    void* out_values, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vts_topk_page_table_transform -- top-k over row windows with the compact
+ * page-table transform (FlashInfer page-size PR body quoted on the SGLang
+ * PR #33237 page, "Description"; `lengths` / `row_starts` as in SGLang's
+ * fast_topk_v2, TopK_Ops page, I/O contract).
+ *
+ * scores       device, dtype, num_rows rows, `width` columns, `row_stride`
+ *              elements apart (row_stride >= width).
+ * lengths      device int32[num_rows]: valid length of each row's window.
+ * row_starts   device int32[num_rows] or NULL (all 0): first column of each
+ *              row's window, in score elements.  The window is
+ *              [row_start, row_start + n) with n = clamp(length, 0,
+ *              width - row_start); a start outside [0, width] gives n = 0.
+ * src_page_table device int32, num_rows rows of page_table_width entries,
+ *              page_table_stride entries apart.
+ * page_table_row_starts device int32[num_rows] or NULL: first page-table entry
+ *              of each row, in page-table entries.  NULL means the row start
+ *              (row_starts, or 0); when page_size > 1 and row_starts is given
+ *              it is required.
+ * page_size    1 <= page_size <= 2^30.
+ * top_k        1 <= top_k <= 2048.
+ * out          device int32[num_rows, top_k], 16-byte aligned: for each
+ *              selected window-relative index idx,
+ *                src_page_table[r, pt_start + idx / page_size] * page_size
+ *                  + idx % page_size,
+ *              and -1 in unused slots.  A page-table entry outside
+ *              [0, page_table_width) also yields -1.
+ * out_raw_indices device int32[num_rows, top_k] or NULL: the window-relative
+ *              indices themselves, positionally aligned with `out`, -1 in
+ *              unused slots.  Must not overlap `out`.
+ * workspace    as for vts_topk_varlen, sized by vts_page_transform_workspace_bytes.
+ */
+int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows,
+                                  int64_t width, int64_t row_stride, const int32_t* lengths,
+                                  const int32_t* row_starts, const int32_t* src_page_table,
+                                  int64_t page_table_stride, int64_t page_table_width,
+                                  const int32_t* page_table_row_starts, int32_t page_size,
+                                  int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Aliases with the operation names of the pages. */
+int topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
+                int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
+                void* out_values, void* workspace, size_t workspace_bytes, void* stream);
+int topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                              int64_t row_stride, const int32_t* lengths,
+                              const int32_t* row_starts, const int32_t* src_page_table,
+                              int64_t page_table_stride, int64_t page_table_width,
+                              const int32_t* page_table_row_starts, int32_t page_size,
+                              int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable text of a vts_status. */
+const char* vts_status_string(int status);
+
+/* Event counters kept in a workspace, copied to `out` (host, >= 4 entries)
+ * with a synchronous copy on `stream`, then cleared:
+ *   out[0]  workgroups whose candidates overflowed and were re-filtered
+ *   out[1]  rows whose sampled threshold kept fewer than top_k candidates
+ *           and that were re-selected over the whole row
+ *   out[2]  merges of split rows too large for on-chip memory
+ *   out[3]  reserved (0) */
+int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* stream);
+
+/* Tuning and test switches (process-wide; not thread-safe).  None of them
+ * changes results, only which internal path computes them.
+ *   VTS_TUNE_NSPLIT       workgroups per long row (0 = automatic, 1..32)
+ *   VTS_TUNE_FORCE_PATH   0 normal, 1 every chunk uses the compaction filter,
+ *                         2 every row is re-selected over the whole row
+ *   VTS_TUNE_LDS_SLOTS    on-chip candidate slots before spilling to the
+ *                         workspace (0 = default; 64..4096)
+ *   VTS_TUNE_SPILL_SLOTS  candidate slots per workgroup including the
+ *                         on-chip ones before a chunk is re-filtered (0 =
+ *                         default; up to the default, which sizes the workspace)
+ *   VTS_TUNE_SAMPLE_SIGMA safety margin of the sampled threshold in tenths of
+ *                         a standard deviation (0 = default 55)
+ *   VTS_TUNE_MIN_CHUNK    valid columns per workgroup below which a row is not
+ *                         split further (0 = default 16384; 256..2^20)
+ * The workspace size follows the split count in force when it is queried.
+ * Returns VTS_OK or VTS_ERR_INVALID for an unknown key or value. */
+enum {
+    VTS_TUNE_NSPLIT = 1,
+    VTS_TUNE_FORCE_PATH = 2,
+    VTS_TUNE_LDS_SLOTS = 3,
+    VTS_TUNE_SPILL_SLOTS = 4,
+    VTS_TUNE_SAMPLE_SIGMA = 5,
+    VTS_TUNE_MIN_CHUNK = 6
+};
+int vts_set_tuning(int32_t key, int64_t value);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VTS_H */

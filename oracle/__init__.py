@@ -80,7 +80,9 @@ def _p(a, ctype):
 
 
 def default_threads() -> int:
-    return max(1, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count() or 1)
+    """Host threads for the oracle: the visible cores, at most 16."""
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(16, n))
 
 
 def valid_len(seq_len: int, next_n: int, t: int, compress_ratio: int, width: int) -> int:

@@ -1,0 +1,180 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/vts.h declares, and its host-side argument checks return the documented
+status codes before any HIP call (fake pointers are never dereferenced)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import varlen_top_select_amd as vts
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vts.h")
+
+OK, WARN, INVALID, UNSUPPORTED, WORKSPACE, HIP = 0, 1, -1, -2, -3, -4
+A = 1 << 20  # fake, 16-byte aligned "device" addresses (never touched)
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vts.LIB_PATH):
+        from varlen_top_select_amd import build
+        build.build()
+    return vts.library()
+
+
+def test_header_declares_the_two_operations():
+    names = declared_functions()
+    for n in ("vts_topk_varlen", "vts_topk_page_table_transform", "topk_varlen",
+              "topk_page_table_transform", "vts_topk_varlen_workspace_bytes",
+              "vts_page_transform_workspace_bytes", "vts_workspace_init", "vts_status_string",
+              "vts_workspace_stats", "vts_set_tuning"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", vts.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in declared_functions():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_probe_library_exports_its_header():
+    probe_h = os.path.join(ROOT, "include", "vts_probe.h")
+    path = os.path.join(ROOT, "varlen_top_select_amd", "libvts_probe.so")
+    if not os.path.exists(path):
+        from varlen_top_select_amd import build
+        build.build()
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    names = declared_functions(probe_h)
+    assert names == ["vts_probe_copy", "vts_probe_read"]
+    for n in names:
+        assert n in exported
+
+
+def test_every_header_is_covered():
+    heads = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert heads == ["vts.h", "vts_probe.h"]
+
+
+def test_status_strings(lib):
+    for s in (OK, WARN, INVALID, UNSUPPORTED, WORKSPACE, HIP):
+        assert lib.vts_status_string(s)
+    assert lib.vts_status_string(12345) == b"unknown status"
+
+
+def test_workspace_size_is_a_pure_function_of_shape(lib):
+    a = lib.vts_topk_varlen_workspace_bytes(1024, 262144, 2048, 0)
+    b = lib.vts_topk_varlen_workspace_bytes(1024, 262144, 2048, 0)
+    assert a == b and a >= 256 and a % 256 == 0
+    assert lib.vts_topk_varlen_workspace_bytes(0, 10, 1, 0) == 256
+    # more rows never need less
+    assert lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0) <= \
+        lib.vts_topk_varlen_workspace_bytes(128, 163840, 2048, 0)
+
+
+def _varlen(lib, **kw):
+    args = dict(logits=A, dtype=0, num_rows=8, width=4096, row_stride=4096, seq_lens=A,
+                top_k=512, next_n=1, cr=1, pre_idx=None, out=A, vals=None, ws=A,
+                ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return lib.vts_topk_varlen(args["logits"], args["dtype"], args["num_rows"], args["width"],
+                               args["row_stride"], args["seq_lens"], args["top_k"], args["next_n"],
+                               args["cr"], args["pre_idx"], args["out"], args["vals"], args["ws"],
+                               args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dtype=3), INVALID),
+    (dict(dtype=-1), INVALID),
+    (dict(num_rows=-1), INVALID),
+    (dict(width=0), INVALID),
+    (dict(row_stride=100), INVALID),
+    (dict(top_k=0), INVALID),
+    (dict(top_k=2049), UNSUPPORTED),
+    (dict(width=1 << 31, row_stride=1 << 31), UNSUPPORTED),
+    (dict(logits=None), INVALID),
+    (dict(logits=A + 2), INVALID),          # not aligned to 4-byte fp32 elements
+    (dict(seq_lens=None), INVALID),
+    (dict(next_n=0), INVALID),
+    (dict(next_n=3), INVALID),              # 8 rows not a multiple of 3
+    (dict(cr=0), INVALID),
+    (dict(out=None), INVALID),
+    (dict(out=A + 4), INVALID),             # not 16-byte aligned
+    (dict(vals=A + 8), INVALID),
+    (dict(vals=A + 4096), INVALID),         # overlaps out_indices (8 x 512 x 4 bytes)
+    (dict(ws=None), WORKSPACE),
+    (dict(ws=A + 8), WORKSPACE),
+    (dict(ws_bytes=16), WORKSPACE),
+])
+def test_varlen_argument_errors(lib, kw, want):
+    assert _varlen(lib, **kw) == want
+
+
+def test_varlen_zero_rows_is_a_no_op(lib):
+    assert _varlen(lib, num_rows=0, logits=None, seq_lens=None, out=None, ws=None) == OK
+
+
+def _transform(lib, **kw):
+    args = dict(scores=A, dtype=2, num_rows=4, width=1024, row_stride=1040, lengths=A,
+                row_starts=None, pt=A, pt_stride=32, pt_width=32, ptrs=None, page_size=64,
+                top_k=256, out=A, raw=None, ws=A, ws_bytes=1 << 40, stream=None)
+    args.update(kw)
+    return lib.vts_topk_page_table_transform(
+        args["scores"], args["dtype"], args["num_rows"], args["width"], args["row_stride"],
+        args["lengths"], args["row_starts"], args["pt"], args["pt_stride"], args["pt_width"],
+        args["ptrs"], args["page_size"], args["top_k"], args["out"], args["raw"], args["ws"],
+        args["ws_bytes"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(page_size=0), INVALID),
+    (dict(page_size=(1 << 30) + 1), INVALID),
+    (dict(pt_width=0), INVALID),
+    (dict(pt_stride=16), INVALID),
+    (dict(row_starts=A), INVALID),          # page_size > 1 with row_starts needs ptrs
+    (dict(lengths=None), INVALID),
+    (dict(pt=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(raw=A + 8), INVALID),
+    (dict(raw=A + 1024), INVALID),          # overlaps out (4 x 256 x 4 bytes)
+    (dict(scores=A + 1), INVALID),          # not aligned to 2-byte fp16 elements
+    (dict(top_k=4096), UNSUPPORTED),
+    (dict(ws_bytes=0), WORKSPACE),
+])
+def test_transform_argument_errors(lib, kw, want):
+    assert _transform(lib, **kw) == want
+
+
+def test_tuning_switches(lib):
+    assert lib.vts_set_tuning(99, 0) == INVALID
+    assert lib.vts_set_tuning(vts.TUNE_NSPLIT, 33) == INVALID
+    assert lib.vts_set_tuning(vts.TUNE_FORCE_PATH, 3) == INVALID
+    assert lib.vts_set_tuning(vts.TUNE_LDS_SLOTS, 10) == INVALID
+    for key in (vts.TUNE_NSPLIT, vts.TUNE_FORCE_PATH, vts.TUNE_LDS_SLOTS, vts.TUNE_SPILL_SLOTS,
+                vts.TUNE_SAMPLE_SIGMA):
+        assert lib.vts_set_tuning(key, 0) == OK
+    # the forced split count changes the workspace size accordingly
+    base = lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0)
+    assert lib.vts_set_tuning(vts.TUNE_NSPLIT, 1) == OK
+    one = lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0)
+    assert lib.vts_set_tuning(vts.TUNE_NSPLIT, 0) == OK
+    assert one < base
+
+
+def test_valid_call_without_a_gpu_reports_hip_error(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; fake pointers must not reach a launch")
+    assert _varlen(lib) == HIP

@@ -1,0 +1,297 @@
+// vts_api.hip -- C ABI of the top-k library: argument checks (host only, before
+// any HIP call), the launch plan (a pure function of the static shape, so a
+// call can be captured in a HIP graph), workspace sizing and the launch.
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/vts.h"
+#include "vts_device.hpp"
+#include "vts_internal.h"
+
+namespace {
+
+using namespace vts;
+
+// Units of work per launch the plan aims for: four workgroups per compute unit
+// of an MI355X (256 CUs).  A fixed constant keeps the plan -- and the workspace
+// size -- independent of the device query.
+constexpr int64_t TARGET_UNITS = 4 * 256;
+// A row gets at most one workgroup per MIN_CHUNK valid columns.
+constexpr int32_t MIN_CHUNK = 16384;
+
+struct Tuning {
+    int32_t nsplit = 0;
+    int32_t force_path = 0;
+    int32_t lds_slots = 0;
+    int32_t spill_slots = 0;
+    int32_t sigma_tenths = 0;
+    int32_t min_chunk = 0;
+} g_tune;
+
+int32_t plan_nsplit(int64_t num_rows, int64_t width) {
+    if (g_tune.nsplit > 0) return g_tune.nsplit;
+    if (num_rows <= 0) return 1;
+    int64_t ns = (TARGET_UNITS + num_rows - 1) / num_rows;
+    const int64_t by_width = (width + MIN_CHUNK - 1) / MIN_CHUNK;
+    if (ns > by_width) ns = by_width;
+    if (ns > MAX_SPLIT) ns = MAX_SPLIT;
+    if (ns < 1) ns = 1;
+    return (int32_t)ns;
+}
+
+size_t workspace_bytes(int64_t num_rows, int64_t width) {
+    if (num_rows <= 0) return 256;
+    return ws_layout(num_rows, plan_nsplit(num_rows, width)).total;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+}
+
+size_t itemsize(int32_t dtype) { return dtype == VTS_F32 ? 4 : 2; }
+
+// Common checks of the score-row arguments.
+int check_rows(const void* x, int32_t dtype, int64_t num_rows, int64_t width, int64_t row_stride,
+               int32_t top_k) {
+    if (dtype != VTS_F32 && dtype != VTS_BF16 && dtype != VTS_F16) return VTS_ERR_INVALID;
+    if (num_rows < 0 || width < 1 || row_stride < width) return VTS_ERR_INVALID;
+    if (top_k < 1) return VTS_ERR_INVALID;
+    if (top_k > 2048) return VTS_ERR_UNSUPPORTED;
+    if (width > INT32_MAX || num_rows > (int64_t)INT32_MAX / MAX_SPLIT) return VTS_ERR_UNSUPPORTED;
+    if (num_rows > 0 && (x == nullptr || !aligned(x, itemsize(dtype)))) return VTS_ERR_INVALID;
+    return VTS_OK;
+}
+
+int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width) {
+    if (ws == nullptr || !aligned(ws, 16)) return VTS_ERR_WORKSPACE;
+    if (bytes < workspace_bytes(num_rows, width)) return VTS_ERR_WORKSPACE;
+    return VTS_OK;
+}
+
+// gfx950 check, cached per device.
+int check_device() {
+    static std::mutex mu;
+    static int known[64];  // 0 unknown, 1 gfx950, 2 other
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return VTS_ERR_HIP;
+    if (dev < 0 || dev >= 64) return VTS_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VTS_ERR_HIP;
+        known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return known[dev] == 1 ? VTS_OK : VTS_ERR_UNSUPPORTED;
+}
+
+void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
+    const int32_t ns = plan_nsplit(num_rows, width);
+    const WsLayout L = ws_layout(num_rows, ns);
+    char* w = static_cast<char*>(ws);
+    p.nsplit = ns;
+    p.min_chunk = g_tune.min_chunk > 0 ? g_tune.min_chunk : MIN_CHUNK;
+    p.num_units = (int32_t)(num_rows * ns);
+    p.units_per_xcd = (p.num_units + 7) / 8;
+    p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
+    p.wscap = g_tune.spill_slots > 0 ? g_tune.spill_slots : WSCAP;
+    if (p.wscap < p.lds_cap) p.wscap = p.lds_cap;
+    p.force_path = g_tune.force_path;
+    p.sigma = (g_tune.sigma_tenths > 0 ? g_tune.sigma_tenths : 55) / 10.0f;
+    p.ws_stats = reinterpret_cast<uint32_t*>(w + L.stats);
+    p.ws_ticket = reinterpret_cast<uint32_t*>(w + L.ticket);
+    p.ws_count = reinterpret_cast<uint32_t*>(w + L.count);
+    p.ws_key = reinterpret_cast<uint32_t*>(w + L.key);
+    p.ws_idx = reinterpret_cast<uint32_t*>(w + L.idx);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t vts_topk_varlen_workspace_bytes(int64_t num_rows, int64_t width, int32_t, int32_t) {
+    return workspace_bytes(num_rows, width);
+}
+
+size_t vts_page_transform_workspace_bytes(int64_t num_rows, int64_t width, int32_t, int32_t) {
+    return workspace_bytes(num_rows, width);
+}
+
+int vts_workspace_init(void* workspace, size_t bytes, void* stream) {
+    if (workspace == nullptr) return VTS_ERR_WORKSPACE;
+    if (hipMemsetAsync(workspace, 0, bytes, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VTS_ERR_HIP;
+    return VTS_OK;
+}
+
+int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                    int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
+                    int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
+                    void* out_values, void* workspace, size_t workspace_bytes_, void* stream) {
+    int st = check_rows(logits, dtype, num_rows, width, row_stride, top_k);
+    if (st != VTS_OK) return st;
+    if (next_n < 1 || compress_ratio < 1 || num_rows % next_n != 0) return VTS_ERR_INVALID;
+    if (num_rows == 0) return VTS_OK;
+    if (seq_lens == nullptr) return VTS_ERR_INVALID;
+    if (out_indices == nullptr || !aligned(out_indices, 16)) return VTS_ERR_INVALID;
+    if (out_values && !aligned(out_values, 16)) return VTS_ERR_INVALID;
+    const size_t nk = (size_t)num_rows * (size_t)top_k;
+    if (out_values && overlap(out_indices, nk * 4, out_values, nk * itemsize(dtype)))
+        return VTS_ERR_INVALID;
+    int warn = VTS_OK;
+    if (pre_idx && !aligned(pre_idx, 16)) {
+        pre_idx = nullptr;
+        warn = VTS_WARN_HINT_DISCARDED;
+    }
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (st != VTS_OK) return st;
+    st = check_device();
+    if (st != VTS_OK) return st;
+
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.x = logits;
+    p.row_stride = row_stride;
+    p.width = width;
+    p.num_rows = (int32_t)num_rows;
+    p.k = top_k;
+    p.seq_lens = seq_lens;
+    p.next_n = next_n;
+    p.cr = compress_ratio;
+    p.pre_idx = pre_idx;
+    p.out_idx = out_indices;
+    p.out_vals = out_values;
+    fill_plan(p, num_rows, width, workspace);
+    if (launch_varlen(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess) return VTS_ERR_HIP;
+    return warn;
+}
+
+int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows,
+                                  int64_t width, int64_t row_stride, const int32_t* lengths,
+                                  const int32_t* row_starts, const int32_t* src_page_table,
+                                  int64_t page_table_stride, int64_t page_table_width,
+                                  const int32_t* page_table_row_starts, int32_t page_size,
+                                  int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                                  void* workspace, size_t workspace_bytes_, void* stream) {
+    int st = check_rows(scores, dtype, num_rows, width, row_stride, top_k);
+    if (st != VTS_OK) return st;
+    if (page_size < 1 || page_size > (1 << 30)) return VTS_ERR_INVALID;
+    if (page_table_width < 1 || page_table_stride < page_table_width) return VTS_ERR_INVALID;
+    // FlashInfer page-size PR body: with page_size > 1 and row_starts given the
+    // page-table starts must be explicit.
+    if (page_size > 1 && row_starts && !page_table_row_starts) return VTS_ERR_INVALID;
+    if (num_rows == 0) return VTS_OK;
+    if (lengths == nullptr || src_page_table == nullptr) return VTS_ERR_INVALID;
+    if (out == nullptr || !aligned(out, 16)) return VTS_ERR_INVALID;
+    if (out_raw_indices && !aligned(out_raw_indices, 16)) return VTS_ERR_INVALID;
+    const size_t nk = (size_t)num_rows * (size_t)top_k;
+    if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (st != VTS_OK) return st;
+    st = check_device();
+    if (st != VTS_OK) return st;
+
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.x = scores;
+    p.row_stride = row_stride;
+    p.width = width;
+    p.num_rows = (int32_t)num_rows;
+    p.k = top_k;
+    p.next_n = 1;
+    p.cr = 1;
+    p.lengths = lengths;
+    p.row_starts = row_starts;
+    p.pt = src_page_table;
+    p.pt_stride = page_table_stride;
+    p.pt_width = page_table_width;
+    p.ptrs = page_table_row_starts;
+    p.page_size = page_size;
+    p.out_idx = out;
+    p.out_raw = out_raw_indices;
+    fill_plan(p, num_rows, width, workspace);
+    if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VTS_ERR_HIP;
+    return VTS_OK;
+}
+
+int topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
+                int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
+                void* out_values, void* workspace, size_t workspace_bytes_, void* stream) {
+    return vts_topk_varlen(logits, dtype, num_rows, width, row_stride, seq_lens, top_k, next_n,
+                           compress_ratio, pre_idx, out_indices, out_values, workspace,
+                           workspace_bytes_, stream);
+}
+
+int topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                              int64_t row_stride, const int32_t* lengths,
+                              const int32_t* row_starts, const int32_t* src_page_table,
+                              int64_t page_table_stride, int64_t page_table_width,
+                              const int32_t* page_table_row_starts, int32_t page_size,
+                              int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                              void* workspace, size_t workspace_bytes_, void* stream) {
+    return vts_topk_page_table_transform(scores, dtype, num_rows, width, row_stride, lengths,
+                                         row_starts, src_page_table, page_table_stride,
+                                         page_table_width, page_table_row_starts, page_size, top_k,
+                                         out, out_raw_indices, workspace, workspace_bytes_, stream);
+}
+
+const char* vts_status_string(int status) {
+    switch (status) {
+        case VTS_OK: return "ok";
+        case VTS_WARN_HINT_DISCARDED: return "pre_idx unusable (misaligned); ran without a hint";
+        case VTS_ERR_INVALID: return "invalid argument";
+        case VTS_ERR_UNSUPPORTED: return "unsupported request or device";
+        case VTS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case VTS_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* stream) {
+    if (workspace == nullptr || out == nullptr || count < 1) return VTS_ERR_INVALID;
+    if (count > 4) count = 4;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(out, workspace, (size_t)count * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return VTS_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return VTS_ERR_HIP;
+    if (hipMemsetAsync(workspace, 0, 16, s) != hipSuccess) return VTS_ERR_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return VTS_ERR_HIP;
+    return VTS_OK;
+}
+
+int vts_set_tuning(int32_t key, int64_t value) {
+    switch (key) {
+        case VTS_TUNE_NSPLIT:
+            if (value < 0 || value > MAX_SPLIT) return VTS_ERR_INVALID;
+            g_tune.nsplit = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_FORCE_PATH:
+            if (value < 0 || value > 2) return VTS_ERR_INVALID;
+            g_tune.force_path = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_LDS_SLOTS:
+            if (value != 0 && (value < 64 || value > CAP)) return VTS_ERR_INVALID;
+            g_tune.lds_slots = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_SPILL_SLOTS:
+            if (value != 0 && (value < 64 || value > WSCAP)) return VTS_ERR_INVALID;
+            g_tune.spill_slots = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_SAMPLE_SIGMA:
+            if (value < 0 || value > 1000) return VTS_ERR_INVALID;
+            g_tune.sigma_tenths = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_MIN_CHUNK:
+            if (value != 0 && (value < 256 || value > (1 << 20))) return VTS_ERR_INVALID;
+            g_tune.min_chunk = (int32_t)value;
+            return VTS_OK;
+    }
+    return VTS_ERR_INVALID;
+}
+
+}  // extern "C"

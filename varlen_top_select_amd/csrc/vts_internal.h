@@ -1,0 +1,79 @@
+// vts_internal.h -- kernel parameter block and launch entry points shared by
+// the kernels (vts_kernels.hip) and the C ABI (vts_api.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace vts {
+
+// Candidate slots per workgroup in the workspace (on-chip slots included).
+constexpr int WSCAP = 8192;
+
+struct Params {
+    // score rows
+    const void* x;
+    int64_t row_stride;  // elements
+    int64_t width;
+    int32_t num_rows;
+    int32_t k;
+    // topk_varlen rows
+    const int32_t* seq_lens;
+    int32_t next_n;
+    int32_t cr;
+    const int32_t* pre_idx;  // reserved for the hint; may be null
+    // page-transform rows
+    const int32_t* lengths;
+    const int32_t* row_starts;
+    const int32_t* pt;
+    int64_t pt_stride;
+    int64_t pt_width;
+    const int32_t* ptrs;
+    int32_t page_size;
+    // outputs
+    int32_t* out_idx;  // topk_varlen: indices; transform: translated `out`
+    void* out_vals;    // topk_varlen values or null
+    int32_t* out_raw;  // transform raw indices or null
+    // plan
+    int32_t nsplit;     // workgroups per row (1..MAX_SPLIT)
+    int32_t min_chunk;  // a row gets ceil(n / min_chunk) workgroups, at most nsplit
+    int32_t num_units;  // num_rows * nsplit
+    int32_t units_per_xcd;
+    int32_t lds_cap;    // on-chip candidate slots used before spilling (<= CAP)
+    int32_t wscap;      // candidate slots per workgroup before re-filtering (<= WSCAP)
+    int32_t force_path;
+    float sigma;        // safety margin of the sampled threshold, in standard deviations
+    // workspace
+    uint32_t* ws_stats;
+    uint32_t* ws_ticket;
+    uint32_t* ws_count;
+    uint32_t* ws_key;
+    uint32_t* ws_idx;
+};
+
+enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };
+
+// Workspace layout (bytes from the base): stats, tickets, counts, keys, indices.
+struct WsLayout {
+    size_t stats, ticket, count, key, idx, total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
+    WsLayout L;
+    const size_t units = (size_t)num_rows * (size_t)nsplit;
+    L.stats = 0;
+    L.ticket = 256;
+    L.count = L.ticket + align256((size_t)num_rows * 4);
+    L.key = L.count + align256(units * 4);
+    L.idx = L.key + align256(units * WSCAP * 4);
+    L.total = L.idx + align256(units * WSCAP * 4);
+    return L;
+}
+
+hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream);
+hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream);
+
+}  // namespace vts
