@@ -238,6 +238,8 @@ def main() -> int:
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only-steps", action="store_true",
                     help="time the steps only (for profiler runs)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MB",
+                    help="also run one plain copy of MB megabytes (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -312,8 +314,22 @@ def main() -> int:
                      "valid_bytes_frac_of_peak": round(valid / (kern_us.mean() * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                      "kernel_source_hash": src_hash},
         "events": {"refiltered_workgroups": stats[0], "whole_row_reselections": stats[1],
-                   "offchip_merges": stats[2]},
+                   "workspace_compactions": stats[2],
+                   "lower_rung_readbacks": stats[3]},
     }
+    if args.calibrate_copy:
+        nb = args.calibrate_copy << 20
+        src = torch.ones(nb // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        plib = ctypes.CDLL(os.path.join(ROOT, "varlen_top_select_amd", "libvts_probe.so"))
+        plib.vts_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+        Flusher(torch)()
+        plib.vts_probe_copy(dst.data_ptr(), src.data_ptr(), nb,
+                            torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        line["calibration_copy_bytes"] = nb
+        del src, dst
     if args.only_steps:
         print(json.dumps(line), flush=True)
         return 0

@@ -47,8 +47,8 @@ typedef enum {
      * (FlashInfer top_k_varlen doc, "raises ValueError"). */
     VTS_ERR_INVALID = -1,
     /* the request is valid but outside what this library implements:
-     * top_k outside [1, 2048], width above 2^31 - 1, or a device other than
-     * gfx950. */
+     * top_k outside [1, 2048], a row of width columns taking 2^31 bytes or
+     * more, or a device other than gfx950. */
     VTS_ERR_UNSUPPORTED = -2,
     /* workspace pointer null or smaller than the matching *_workspace_bytes(). */
     VTS_ERR_WORKSPACE = -3,
@@ -175,8 +175,10 @@ const char* vts_status_string(int status);
  *   out[0]  workgroups whose candidates overflowed and were re-filtered
  *   out[1]  rows whose sampled threshold kept fewer than top_k candidates
  *           and that were re-selected over the whole row
- *   out[2]  merges of split rows too large for on-chip memory
- *   out[3]  reserved (0) */
+ *   out[2]  rows whose candidates outgrew on-chip memory and were compacted
+ *           back from the workspace
+ *   out[3]  rows whose upper-rung candidates were fewer than top_k, so that
+ *           the lower rung was read back */
 int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* stream);
 
 /* Tuning and test switches (process-wide; not thread-safe).  None of them
@@ -186,11 +188,12 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *                         2 every row is re-selected over the whole row
  *   VTS_TUNE_LDS_SLOTS    on-chip candidate slots before spilling to the
  *                         workspace (0 = default; 64..4096)
- *   VTS_TUNE_SPILL_SLOTS  candidate slots per workgroup including the
- *                         on-chip ones before a chunk is re-filtered (0 =
- *                         default; up to the default, which sizes the workspace)
- *   VTS_TUNE_SAMPLE_SIGMA safety margin of the sampled threshold in tenths of
- *                         a standard deviation (0 = default 55)
+ *   VTS_TUNE_SPILL_SLOTS  workspace candidate slots per workgroup and rung
+ *                         before a chunk is re-filtered (0 = default; 64..8192)
+ *   VTS_TUNE_SAMPLE_SIGMA margin of the safe threshold rung in tenths of a
+ *                         standard deviation of the sample count (0 = 55)
+ *   VTS_TUNE_LIKELY_SIGMA margin of the likely rung, same unit (0 = 20; a
+ *                         value >= the safe margin merges the two rungs)
  *   VTS_TUNE_MIN_CHUNK    valid columns per workgroup below which a row is not
  *                         split further (0 = default 16384; 256..2^20)
  * The workspace size follows the split count in force when it is queried.
@@ -201,7 +204,8 @@ enum {
     VTS_TUNE_LDS_SLOTS = 3,
     VTS_TUNE_SPILL_SLOTS = 4,
     VTS_TUNE_SAMPLE_SIGMA = 5,
-    VTS_TUNE_MIN_CHUNK = 6
+    VTS_TUNE_MIN_CHUNK = 6,
+    VTS_TUNE_LIKELY_SIGMA = 7
 };
 int vts_set_tuning(int32_t key, int64_t value);
 

@@ -68,6 +68,10 @@ PATHS = {
     "split3_fallback": dict(nsplit=3, min_chunk=4096, force=2),
     "split32": dict(nsplit=32, min_chunk=256),
     "tight_sigma": dict(sigma=1),
+    "one_rung": dict(likely=55),
+    "high_likely_rung": dict(likely=1, sigma=55),
+    "split8_high_likely_rung": dict(nsplit=8, min_chunk=1024, likely=1),
+    "split8_lo_overflow": dict(nsplit=8, min_chunk=1024, likely=1, spill=64),
 }
 
 REDUCED = {1: dict(rows=4), 2: dict(rows=8), 3: dict(rows=8, width=65536), 4: dict(rows=32),

@@ -104,6 +104,8 @@ def _varlen(lib, **kw):
     (dict(top_k=0), INVALID),
     (dict(top_k=2049), UNSUPPORTED),
     (dict(width=1 << 31, row_stride=1 << 31), UNSUPPORTED),
+    (dict(width=1 << 29, row_stride=1 << 29), UNSUPPORTED),   # 2^31 bytes of fp32
+    (dict(dtype=1, width=1 << 30, row_stride=1 << 30), UNSUPPORTED),
     (dict(logits=None), INVALID),
     (dict(logits=A + 2), INVALID),          # not aligned to 4-byte fp32 elements
     (dict(seq_lens=None), INVALID),

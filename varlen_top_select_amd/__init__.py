@@ -28,6 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libvts.so")
 OK, WARN_HINT_DISCARDED = 0, 1
 TUNE_NSPLIT, TUNE_FORCE_PATH, TUNE_LDS_SLOTS, TUNE_SPILL_SLOTS, TUNE_SAMPLE_SIGMA = 1, 2, 3, 4, 5
 TUNE_MIN_CHUNK = 6
+TUNE_LIKELY_SIGMA = 7
 
 _DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
@@ -47,8 +48,7 @@ def library():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m varlen_top_select_amd.build`"
-                           " (or __graft_entry__.build())")
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m varlen_top_select_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.vts_topk_varlen.restype = ctypes.c_int
@@ -222,7 +222,8 @@ def set_tuning(key: int, value: int) -> None:
 
 
 def workspace_stats(workspace: torch.Tensor, stream=None) -> list[int]:
-    """[re-filtered workgroups, whole-row re-selections, off-chip merges, 0]; clears them."""
+    """[re-filtered workgroups, whole-row re-selections, workspace compactions,
+    lower-rung read-backs]; clears them."""
     out = (ctypes.c_uint32 * 4)()
     _check("vts_workspace_stats", library().vts_workspace_stats(
         workspace.data_ptr(), out, 4, _stream_ptr(stream, workspace.device)))

@@ -17,8 +17,10 @@ using namespace vts;
 // of an MI355X (256 CUs).  A fixed constant keeps the plan -- and the workspace
 // size -- independent of the device query.
 constexpr int64_t TARGET_UNITS = 4 * 256;
-// A row gets at most one workgroup per MIN_CHUNK valid columns.
-constexpr int32_t MIN_CHUNK = 16384;
+// A row gets at most one workgroup per MIN_CHUNK valid columns: below about
+// 32K columns a split's fixed costs (its own sample and the merge) outweigh
+// the shorter stream (measured on the five benchmark shapes).
+constexpr int32_t MIN_CHUNK = 32768;
 
 struct Tuning {
     int32_t nsplit = 0;
@@ -27,6 +29,7 @@ struct Tuning {
     int32_t spill_slots = 0;
     int32_t sigma_tenths = 0;
     int32_t min_chunk = 0;
+    int32_t likely_tenths = 0;
 } g_tune;
 
 int32_t plan_nsplit(int64_t num_rows, int64_t width) {
@@ -62,6 +65,8 @@ int check_rows(const void* x, int32_t dtype, int64_t num_rows, int64_t width, in
     if (top_k < 1) return VTS_ERR_INVALID;
     if (top_k > 2048) return VTS_ERR_UNSUPPORTED;
     if (width > INT32_MAX || num_rows > (int64_t)INT32_MAX / MAX_SPLIT) return VTS_ERR_UNSUPPORTED;
+    // a row is streamed with 32-bit byte offsets
+    if (width * (int64_t)itemsize(dtype) > (int64_t)INT32_MAX) return VTS_ERR_UNSUPPORTED;
     if (num_rows > 0 && (x == nullptr || !aligned(x, itemsize(dtype)))) return VTS_ERR_INVALID;
     return VTS_OK;
 }
@@ -97,13 +102,21 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
     p.num_units = (int32_t)(num_rows * ns);
     p.units_per_xcd = (p.num_units + 7) / 8;
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
-    p.wscap = g_tune.spill_slots > 0 ? g_tune.spill_slots : WSCAP;
-    if (p.wscap < p.lds_cap) p.wscap = p.lds_cap;
+    p.hi_cap = HI_SLOTS;
+    p.lo_cap = LO_SLOTS;
+    if (g_tune.spill_slots > 0) {
+        p.hi_cap = g_tune.spill_slots;
+        p.lo_cap = g_tune.spill_slots < LO_SLOTS ? g_tune.spill_slots : LO_SLOTS;
+    }
+    if (p.hi_cap < p.lds_cap) p.hi_cap = p.lds_cap;
     p.force_path = g_tune.force_path;
     p.sigma = (g_tune.sigma_tenths > 0 ? g_tune.sigma_tenths : 55) / 10.0f;
+    p.sigma2 = (g_tune.likely_tenths > 0 ? g_tune.likely_tenths : 20) / 10.0f;
+    if (p.sigma2 > p.sigma) p.sigma2 = p.sigma;
     p.ws_stats = reinterpret_cast<uint32_t*>(w + L.stats);
     p.ws_ticket = reinterpret_cast<uint32_t*>(w + L.ticket);
     p.ws_count = reinterpret_cast<uint32_t*>(w + L.count);
+    p.ws_count_lo = reinterpret_cast<uint32_t*>(w + L.count_lo);
     p.ws_key = reinterpret_cast<uint32_t*>(w + L.key);
     p.ws_idx = reinterpret_cast<uint32_t*>(w + L.idx);
 }
@@ -279,12 +292,16 @@ int vts_set_tuning(int32_t key, int64_t value) {
             g_tune.lds_slots = (int32_t)value;
             return VTS_OK;
         case VTS_TUNE_SPILL_SLOTS:
-            if (value != 0 && (value < 64 || value > WSCAP)) return VTS_ERR_INVALID;
+            if (value != 0 && (value < 64 || value > HI_SLOTS)) return VTS_ERR_INVALID;
             g_tune.spill_slots = (int32_t)value;
             return VTS_OK;
         case VTS_TUNE_SAMPLE_SIGMA:
             if (value < 0 || value > 1000) return VTS_ERR_INVALID;
             g_tune.sigma_tenths = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_LIKELY_SIGMA:
+            if (value < 0 || value > 1000) return VTS_ERR_INVALID;
+            g_tune.likely_tenths = (int32_t)value;
             return VTS_OK;
         case VTS_TUNE_MIN_CHUNK:
             if (value != 0 && (value < 256 || value > (1 << 20))) return VTS_ERR_INVALID;

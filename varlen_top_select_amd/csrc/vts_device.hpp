@@ -14,13 +14,14 @@ namespace vts {
 
 constexpr int NT = 256;               // threads per workgroup: 4 wave64
 constexpr int WAVES = NT / 64;
-constexpr int CAP = 4096;             // on-chip candidate slots per workgroup
+constexpr int CAP = 3840;             // on-chip candidate slots per workgroup
+constexpr int STAGE = 96;             // staged 16-byte vectors per wave
+constexpr int STAGE_DRAIN = 32;       // a wave drains once this many are staged
 constexpr int SAMPLE = 4096;          // sampled keys per row: 64 blocks of 64 columns
 constexpr int SAMPLE_BLOCK = 64;
 constexpr int SAMPLE_BLOCKS = SAMPLE / SAMPLE_BLOCK;
 constexpr int SPT = SAMPLE / NT;      // sampled keys per thread (16)
 constexpr int MAX_SPLIT = 32;         // workgroups per row, at most
-constexpr int U = 4;                  // 16-byte vectors per thread per streaming step
 
 enum Dtype : int { F32 = 0, BF16 = 1, F16 = 2 };
 
@@ -40,28 +41,39 @@ template <class T>
 __device__ __forceinline__ void gstore(T* p, T v) {
     *(VTS_GLOBAL T*)p = v;
 }
+// p[i] = v with a 32-bit byte offset from the (wave-uniform) base, which lets
+// the store take the scalar-base + 32-bit vector-offset address form
+__device__ __forceinline__ void gstore_at(uint32_t* p, uint32_t i, uint32_t v) {
+    *(VTS_GLOBAL uint32_t*)((VTS_GLOBAL char*)p + (i << 2)) = v;
+}
 __device__ __forceinline__ uint32_t gatomic_add(uint32_t* p, uint32_t v) {
     return __hip_atomic_fetch_add((VTS_GLOBAL uint32_t*)p, v, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// U: 16-byte vectors per thread per streaming step.  Two steps are in
+// registers at once (one being filtered, one in flight), and the filter keeps
+// a pass mask per step, so U is sized to stay under 128 VGPRs (4 waves/SIMD).
 template <int DT> struct Traits;
 template <> struct Traits<F32> {
     using raw_t = uint32_t;
     static constexpr int BITS = 32;
     static constexpr int VE = 4;  // elements per 16-byte vector
+    static constexpr int U = 6;
     static constexpr uint32_t PAD = 0xFF7FFFFFu;  // -FLT_MAX
 };
 template <> struct Traits<BF16> {
     using raw_t = uint16_t;
     static constexpr int BITS = 16;
     static constexpr int VE = 8;
+    static constexpr int U = 4;
     static constexpr uint32_t PAD = 0xFF7Fu;  // lowest finite bf16
 };
 template <> struct Traits<F16> {
     using raw_t = uint16_t;
     static constexpr int BITS = 16;
     static constexpr int VE = 8;
+    static constexpr int U = 4;
     static constexpr uint32_t PAD = 0xFBFFu;  // lowest finite fp16
 };
 
@@ -111,37 +123,102 @@ __device__ __forceinline__ uint32_t wave_ticket(uint32_t* counter, bool want, ui
     return base + mbcnt(mask);
 }
 
-// Shared state of one workgroup.
+constexpr int RBITS = 10;              // radix digit width of the selection
+constexpr int NBINS = 1 << RBITS;      // 1024 histogram bins
+// Bin d lives at LDS word d + d/16: one pad word per 16 bins, so the 64 lanes
+// of the scanning wave, each reading 16 consecutive bins, hit distinct banks.
+constexpr int HIST_WORDS = NBINS + NBINS / 16;
+__device__ __forceinline__ uint32_t hslot(uint32_t d) { return d + (d >> 4); }
+
+// Wave-aggregated ticket for variable counts: each lane asks for `cnt` (<= 127)
+// consecutive slots of *counter (LDS); returns the lane's first slot.  The
+// exclusive prefix of the counts is built from bit slices (one ballot and one
+// mbcnt per bit), so only one LDS atomic is issued per wave.  Every lane of the
+// wave must call it.
+__device__ __forceinline__ uint32_t wave_ticket_n(uint32_t* counter, uint32_t cnt) {
+    if (ballot(cnt != 0) == 0) return 0;
+    uint32_t excl = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 7; ++b) {
+        const uint64_t m = ballot((cnt >> b) & 1u);
+        excl += mbcnt(m) << b;
+        tot += (uint32_t)__popcll(m) << b;
+    }
+    uint32_t base = 0;
+    if (lane_id() == 0) base = atomicAdd(counter, tot);
+    return first_lane_value(base) + excl;
+}
+
+// Shared state of one workgroup (at most 40 KB, so four fit on a CU).  The
+// selection histogram and the streaming filter's per-wave staging queues share
+// their space: the queues exist only between two selections, and the
+// histogram is cleared again after them.
 struct Smem {
     uint32_t key[CAP];
     uint32_t idx[CAP];
-    uint32_t hist[256];
+    union {
+        uint32_t hist[HIST_WORDS];
+        struct {
+            u32x4 vec[WAVES * STAGE];  // wave w owns [w * STAGE, (w + 1) * STAGE)
+            uint32_t v[WAVES * STAGE];  // the vectors' indices in the unit's body
+        } stage;
+    };
     uint32_t wsum[WAVES];
-    uint32_t seg_cnt[MAX_SPLIT];
-    uint32_t cand_n;
+    uint32_t wmin[WAVES];
+    uint32_t wmax[WAVES];
+    uint32_t seg_hi[MAX_SPLIT];
+    uint32_t seg_lo[MAX_SPLIT];
+    uint32_t cand_n;  // upper-rung (or compaction-filter) candidates
+    uint32_t lo_n;    // lower-rung candidates
     uint32_t cnt_a, cnt_b;
     uint32_t sel_digit, sel_above;
+    uint32_t sel_digit2, sel_above2;
     uint32_t flag;
     uint32_t total;
 };
 
-// Inclusive prefix sum over the workgroup (thread order).  Contains barriers:
-// every thread must call it.
+// Inclusive scan across the 64 lanes of a wave with DPP: Hillis-Steele inside
+// each 16-lane row (row_shr 1, 2, 4, 8), then row_bcast 15 and 31 carry the
+// row totals forward.  Lanes without a source get `identity`.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v, uint32_t identity, Op op) {
+    const int id = (int)identity;
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xF, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xA, 0xF, false));
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xC, 0xF, false));
+    return v;
+}
+
+// Workgroup barrier that orders LDS accesses only: the wave's own LDS
+// operations complete (lgkmcnt), then s_barrier; the memory clobber keeps the
+// compiler from moving memory accesses across it.  A full __syncthreads (and
+// even an LDS-scoped fence) also waits for every global load still in flight,
+// asynchronous loads into LDS included; this one lets them stay in flight, so
+// it must not be used to publish LDS written by such loads (wait for them
+// first) nor global memory written by other threads (use __syncthreads).
+__device__ __forceinline__ void lds_sync() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+
+// Inclusive prefix sum over the workgroup (thread order).  Contains barriers
+// (LDS-only, as in every helper below): every thread must call it.
 __device__ __forceinline__ uint32_t block_inclusive_scan(Smem& sm, uint32_t v) {
-    const uint32_t lane = lane_id();
+    v = wave_scan(v, 0u, OpAdd());
     const uint32_t w = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t o = __shfl_up(v, d, 64);
-        if (lane >= (uint32_t)d) v += o;
-    }
-    if (lane == 63) sm.wsum[w] = v;
-    __syncthreads();
+    if (lane_id() == 63) sm.wsum[w] = v;
+    lds_sync();
     uint32_t add = 0;
 #pragma unroll
     for (int i = 0; i < WAVES; ++i)
         if ((uint32_t)i < w) add += sm.wsum[i];
-    __syncthreads();
+    lds_sync();
     return v + add;
 }
 
@@ -151,49 +228,206 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(Smem& sm, uint32_t v) {
 __device__ __forceinline__ uint32_t block_sum(Smem& sm, uint32_t v, uint32_t& cand_snapshot) {
     uint32_t incl = block_inclusive_scan(sm, v);
     if (threadIdx.x == NT - 1) sm.total = incl;
-    __syncthreads();
+    lds_sync();
     const uint32_t t = sm.total;
     cand_snapshot = sm.cand_n;
-    __syncthreads();
+    lds_sync();
     return t;
 }
 
-// Exact r-th largest key (1-based rank r) of the key set that `visit`
-// enumerates, by MSB-first 8-bit radix select.  visit(f) must call f(key) once
-// for every key this thread owns (any order, any divergence).  The set must
-// hold at least r keys.  Returns the key K and, in n_greater, how many keys of
-// the set are strictly greater than K (so r - n_greater of the keys equal to K
-// complete the top r).  Every thread must call it; contains barriers.
-template <int BITS, class Visit>
-__device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, uint32_t& kth,
-                                             uint32_t& n_greater) {
-    uint32_t prefix = 0, mask = 0, krem = r, gt = 0;
+// Workgroup-wide min and max (every thread must call; one barrier).  The
+// per-wave slots are rewritten only by the next call, which is separated from
+// this one by other barriers.
+__device__ __forceinline__ void block_minmax(Smem& sm, uint32_t& lo, uint32_t& hi) {
+    lo = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(lo, 0xFFFFFFFFu, OpMin()), 63);
+    hi = (uint32_t)__builtin_amdgcn_readlane((int)wave_scan(hi, 0u, OpMax()), 63);
+    const uint32_t w = threadIdx.x >> 6;
+    if (lane_id() == 0) {
+        sm.wmin[w] = lo;
+        sm.wmax[w] = hi;
+    }
+    lds_sync();
+    lo = sm.wmin[0];
+    hi = sm.wmax[0];
 #pragma unroll
-    for (int shift = BITS - 8; shift >= 0; shift -= 8) {
-        sm.hist[threadIdx.x] = 0;
-        __syncthreads();
+    for (int i = 1; i < WAVES; ++i) {
+        lo = sm.wmin[i] < lo ? sm.wmin[i] : lo;
+        hi = sm.wmax[i] > hi ? sm.wmax[i] : hi;
+    }
+}
+
+// Zeroes the selection histogram; every select leaves it zeroed again.
+__device__ __forceinline__ void hist_clear(Smem& sm) {
+    // unrolled: no loop for the compiler's wait counts to merge over
+#pragma unroll
+    for (int i = 0; i < (HIST_WORDS + NT - 1) / NT; ++i) {
+        const int j = (int)threadIdx.x + i * NT;
+        if (j < HIST_WORDS) sm.hist[j] = 0;
+    }
+}
+
+// Run by the 64 lanes of one wave after a barrier: bins [base, base + 64*PER)
+// hold digit counts (digit d at bin base + d).  For each of the ranks r1 and
+// r2 (1-based, counted from the largest digit; each at most the total) finds
+// the digit holding that rank and the count of the digits above it, then
+// zeroes the bins.  Lane l sums digits 64*PER-1-PER*l down to 64*PER-PER*(l+1);
+// a DPP scan and a ballot name the lane where the count crosses r, then PER
+// lanes read that lane's bins once more and a second scan names the digit.
+template <int PER>
+__device__ __forceinline__ void hist_crossing(Smem& sm, uint32_t base, uint32_t r1, uint32_t r2,
+                                              uint32_t& d1, uint32_t& a1, uint32_t& d2,
+                                              uint32_t& a2) {
+    constexpr uint32_t NB = 64u * PER;
+    const uint32_t l = lane_id();
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sum += sm.hist[hslot(base + NB - 1 - (l * PER + j))];
+    const uint32_t incl = wave_scan(sum, 0u, OpAdd());
+    const uint32_t excl = incl - sum;
+    auto find = [&](uint32_t r, uint32_t& d, uint32_t& a) {
+        const uint64_t m = ballot(incl >= r);
+        const int L = m ? __builtin_ctzll(m) : 63;
+        const uint32_t exL = (uint32_t)__builtin_amdgcn_readlane((int)excl, L);
+        const uint32_t c = l < (uint32_t)PER ? sm.hist[hslot(base + NB - 1 - ((uint32_t)L * PER + l))] : 0u;
+        const uint32_t ic = wave_scan(c, 0u, OpAdd());
+        const uint64_t m2 = ballot(l < (uint32_t)PER && exL + ic >= r);
+        const int J = m2 ? __builtin_ctzll(m2) : PER - 1;
+        d = NB - 1 - ((uint32_t)L * PER + (uint32_t)J);
+        a = exL + (uint32_t)__builtin_amdgcn_readlane((int)(ic - c), J);
+    };
+    find(r1, d1, a1);
+    if (r2 == r1) {
+        d2 = d1;
+        a2 = a1;
+    } else {
+        find(r2, d2, a2);
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) sm.hist[hslot(base + NB - 1 - (l * PER + j))] = 0;
+}
+
+// Radix select over the key set that `visit` enumerates: visit(f) must call
+// f(key) once for every key this thread owns (any order, any divergence).
+// Finds the r-th largest key (1-based; the set must hold at least r keys),
+// resolving its bits from the highest one in which lo and hi differ down to
+// bit `min_bit`, 10 bits per pass.  Keys whose bits above that one differ
+// from lo's are not counted, so every key must share them (lo <= every key
+// <= hi guarantees it).  Returns in kth the key's bits >= min_bit (lower bits
+// zero), so kth is a lower bound of the r-th largest key, and exact when
+// min_bit == 0; n_greater counts the keys whose bits >= min_bit exceed kth's
+// (with min_bit == 0: the keys strictly greater than the r-th largest, so
+// r - n_greater keys equal to it complete the top r).
+// Each pass: every thread adds its matching keys' digits into 1024 LDS bins;
+// after a barrier wave 0 alone finds the digit holding the remaining rank and
+// zeroes the bins; a second barrier publishes the digit.  The histogram must
+// be zero on entry and is zero on exit.  Every thread must call it.
+template <class Visit>
+__device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, uint32_t lo,
+                                             uint32_t hi, int min_bit, uint32_t& kth,
+                                             uint32_t& n_greater) {
+    const uint32_t low_mask = min_bit >= 32 ? 0xFFFFFFFFu : ((1u << min_bit) - 1u);
+    if (((lo ^ hi) & ~low_mask) == 0) {  // all keys share the bits that matter
+        kth = lo & ~low_mask;
+        n_greater = 0;
+        return;
+    }
+    const int hb = 31 - __clz(lo ^ hi);
+    uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    uint32_t prefix = lo & mask;
+    uint32_t krem = r, gt = 0;
+    for (int top = hb; top >= min_bit; top -= RBITS) {
+        int width = top + 1 - min_bit;
+        if (width > RBITS) width = RBITS;
+        const int shift = top + 1 - width;
+        const uint32_t dmask = (1u << width) - 1u;
         visit([&](uint32_t key) {
-            if ((key & mask) == prefix) atomicAdd(&sm.hist[(key >> shift) & 0xFFu], 1u);
+            if ((key & mask) == prefix) atomicAdd(&sm.hist[hslot((key >> shift) & dmask)], 1u);
         });
-        __syncthreads();
-        // thread t holds bin 255 - t, so an inclusive scan counts keys in bins >= 255 - t
-        const uint32_t b = 255u - threadIdx.x;
-        const uint32_t v = sm.hist[b];
-        const uint32_t incl = block_inclusive_scan(sm, v);
-        const uint32_t excl = incl - v;
-        if (excl < krem && incl >= krem) {
-            sm.sel_digit = b;
-            sm.sel_above = excl;
+        lds_sync();
+        if (threadIdx.x < 64) {
+            uint32_t d, a, d2, a2;
+            hist_crossing<NBINS / 64>(sm, 0u, krem, krem, d, a, d2, a2);
+            if (threadIdx.x == 0) {
+                sm.sel_digit = d;
+                sm.sel_above = a;
+            }
         }
-        __syncthreads();
+        lds_sync();
         const uint32_t d = sm.sel_digit, above = sm.sel_above;
         gt += above;
         krem -= above;
         prefix |= d << shift;
-        mask |= 0xFFu << shift;
+        mask |= dmask << shift;
     }
     kth = prefix;
     n_greater = gt;
+}
+
+// Two lower bounds at once: the r1-th and r2-th largest keys of the set that
+// `visit` enumerates (r1 >= r2, each at most the set's size), resolved to
+// their top BITS - 10 + W2 bits.  Pass 1 takes the top 10 bits as the digit
+// (1024 bins) and finds both ranks' digits; pass 2 takes the next W2 bits (at
+// most 9) of the keys in each of those digits, in two 512-bin halves (one if
+// both digits agree).  Histogram zero on entry and exit; every thread calls.
+template <int BITS, int W2, class Visit>
+__device__ __forceinline__ void block_select_pair(Smem& sm, Visit visit, uint32_t r1, uint32_t r2,
+                                                  uint32_t& k1, uint32_t& k2) {
+    static_assert(W2 >= 1 && W2 <= 9 && BITS - RBITS - W2 >= 0, "digit widths");
+    constexpr int S1 = BITS - RBITS, S2 = S1 - W2;
+    constexpr uint32_t M2 = (1u << W2) - 1u;
+    visit([&](uint32_t key) { atomicAdd(&sm.hist[hslot(key >> S1)], 1u); });
+    lds_sync();
+    if (threadIdx.x < 64) {
+        uint32_t d1, a1, d2, a2;
+        hist_crossing<NBINS / 64>(sm, 0u, r1, r2, d1, a1, d2, a2);
+        if (threadIdx.x == 0) {
+            sm.sel_digit = d1;
+            sm.sel_above = a1;
+            sm.sel_digit2 = d2;
+            sm.sel_above2 = a2;
+        }
+    }
+    lds_sync();
+    const uint32_t d1 = sm.sel_digit, d2 = sm.sel_digit2;
+    const uint32_t q1 = r1 - sm.sel_above, q2 = r2 - sm.sel_above2;
+    const uint32_t base2 = d2 == d1 ? 0u : 512u;
+    visit([&](uint32_t key) {
+        const uint32_t d = key >> S1, e = (key >> S2) & M2;
+        if (d == d1) atomicAdd(&sm.hist[hslot(e)], 1u);
+        if (d == d2 && base2) atomicAdd(&sm.hist[hslot(base2 + e)], 1u);
+    });
+    lds_sync();
+    if (threadIdx.x < 64) {
+        constexpr int PER = (1 << W2) / 64 > 0 ? (1 << W2) / 64 : 1;
+        // with W2 < 6 the 64-lane view covers 64 bins; the digits above 2^W2 are zero
+        uint32_t e1, b1, e2, b2, x, y;
+        hist_crossing<PER>(sm, 0u, q1, base2 ? q1 : q2, e1, b1, x, y);
+        if (base2) {
+            hist_crossing<PER>(sm, base2, q2, q2, e2, b2, x, y);
+        } else {
+            e2 = x;
+        }
+        if (threadIdx.x == 0) {
+            sm.sel_digit = (d1 << S1) | (e1 << S2);
+            sm.sel_digit2 = (d2 << S1) | (e2 << S2);
+        }
+    }
+    lds_sync();
+    k1 = sm.sel_digit;
+    k2 = sm.sel_digit2;
+}
+
+// Exact selection with the key range found first (one extra visit).
+template <class Visit>
+__device__ __forceinline__ void block_select_exact(Smem& sm, Visit visit, uint32_t r,
+                                                   uint32_t& kth, uint32_t& n_greater) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    visit([&](uint32_t key) {
+        lo = key < lo ? key : lo;
+        hi = key > hi ? key : hi;
+    });
+    block_minmax(sm, lo, hi);
+    block_select(sm, visit, r, lo, hi, 0, kth, n_greater);
 }
 
 }  // namespace vts

@@ -8,8 +8,13 @@
 
 namespace vts {
 
-// Candidate slots per workgroup in the workspace (on-chip slots included).
-constexpr int WSCAP = 8192;
+// Candidate slots per workgroup in the workspace.  Region layout: slots
+// [0, HI_SLOTS) mirror the upper-rung candidate buffer (the first on-chip slots
+// are copied there only when a split row publishes them), slots
+// [HI_SLOTS, HI_SLOTS + LO_SLOTS) hold the lower-rung candidates.
+constexpr int HI_SLOTS = 8192;
+constexpr int LO_SLOTS = 4096;
+constexpr int WSCAP = HI_SLOTS + LO_SLOTS;
 
 struct Params {
     // score rows
@@ -40,14 +45,17 @@ struct Params {
     int32_t min_chunk;  // a row gets ceil(n / min_chunk) workgroups, at most nsplit
     int32_t num_units;  // num_rows * nsplit
     int32_t units_per_xcd;
-    int32_t lds_cap;    // on-chip candidate slots used before spilling (<= CAP)
-    int32_t wscap;      // candidate slots per workgroup before re-filtering (<= WSCAP)
+    int32_t lds_cap;    // on-chip upper-rung slots used before spilling (<= CAP)
+    int32_t hi_cap;     // upper-rung slots in all (<= HI_SLOTS) before re-filtering
+    int32_t lo_cap;     // lower-rung slots (<= LO_SLOTS) before re-filtering
     int32_t force_path;
-    float sigma;        // safety margin of the sampled threshold, in standard deviations
+    float sigma;        // margin of the safe rung, in standard deviations
+    float sigma2;       // margin of the likely rung (<= sigma)
     // workspace
     uint32_t* ws_stats;
     uint32_t* ws_ticket;
-    uint32_t* ws_count;
+    uint32_t* ws_count;     // upper-rung candidates per unit
+    uint32_t* ws_count_lo;  // lower-rung candidates per unit
     uint32_t* ws_key;
     uint32_t* ws_idx;
 };
@@ -56,7 +64,7 @@ enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };
 
 // Workspace layout (bytes from the base): stats, tickets, counts, keys, indices.
 struct WsLayout {
-    size_t stats, ticket, count, key, idx, total;
+    size_t stats, ticket, count, count_lo, key, idx, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -67,7 +75,8 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
     L.stats = 0;
     L.ticket = 256;
     L.count = L.ticket + align256((size_t)num_rows * 4);
-    L.key = L.count + align256(units * 4);
+    L.count_lo = L.count + align256(units * 4);
+    L.key = L.count_lo + align256(units * 4);
     L.idx = L.key + align256(units * WSCAP * 4);
     L.total = L.idx + align256(units * WSCAP * 4);
     return L;

@@ -7,24 +7,26 @@
 //     top_k_varlen doc, `seq_lens`) or from lengths / row_starts (SGLang
 //     TopK_Ops, fast_topk_v2).  n == 0 and n <= k rows are answered directly
 //     (TensorRT-LLM PR #17821, short-row commit: identity then -1).
-//  2. threshold: a fixed sample of the row (64 blocks of 64 contiguous
-//     columns, or the whole row when it is short) is radix-selected in LDS at a
-//     rank chosen so that, for exchangeable data, at least k row elements
-//     clear the threshold except with negligible probability (the
-//     sample-calibrated threshold of the self-sampling GVR V2 description on
-//     the TensorRT-LLM PR #17821 page).  All workgroups of a row compute the
-//     same threshold.
+//  2. thresholds: a fixed sample of the row (64 blocks of 64 contiguous
+//     columns, or the whole row when it is short) is radix-selected in LDS at
+//     two ranks -- a ladder of two rungs, after the sample-calibrated
+//     thresholds of the self-sampling GVR V2 description on the TensorRT-LLM
+//     PR #17821 page.  The safe rung T is placed so that, for exchangeable
+//     data, at least k row elements clear it except with negligible
+//     probability; the likely rung T2 >= T so that they clear it in most rows.
+//     All workgroups of a row compute the same rungs.
 //  3. filter: one coalesced pass over the unit's columns with 16-byte loads;
-//     keys >= threshold are appended to LDS with wave-aggregated tickets,
-//     spilling to the workspace when LDS is full.  If even the workspace slots
+//     keys >= T2 are appended to LDS and keys in [T, T2) to the workspace,
+//     both with one wave-aggregated ticket per wave and step.  If the slots
 //     run out, the unit is re-filtered with a compaction filter that keeps at
 //     most k candidates at any time (exact for any input, slower).
-//  4. verify: exactness needs at least k candidates over the row (then every
-//     top-k element cleared the threshold).  Otherwise the row is re-selected
-//     over all its columns with the compaction filter (never for
-//     exchangeable data; exactness never rests on the sample).
+//  4. verify: if at least k keys cleared T2, the top k are among them; else,
+//     if at least k cleared T, among those (the lower rung is read back);
+//     else the row is re-selected over all its columns with the compaction
+//     filter (never for exchangeable data: exactness rests on these counts,
+//     never on the sample).
 //  5. select: the k-th largest candidate key K and the count g of keys > K,
-//     by 8-bit radix select in LDS.
+//     by radix select in LDS (10-bit digits from the first differing bit).
 //  6. epilogue: all keys > K and k - g keys == K are written (ties are
 //     interchangeable); indices are window-relative.  The page-table policy
 //     applies the compact transform of the FlashInfer page-size PR body.
@@ -33,6 +35,8 @@
 // candidates to the workspace, then takes a ticket; the last one merges the
 // candidates (steps 4-6) and resets the ticket, leaving the workspace clean.
 // No workgroup ever waits for another.
+
+#include <type_traits>
 
 #include "vts_device.hpp"
 #include "vts_internal.h"
@@ -132,22 +136,32 @@ __device__ __forceinline__ Slice make_slice(const typename Traits<DT>::raw_t* ro
     return s;
 }
 
-// Keys of one streaming step held by a thread: U vectors of VE elements.
-template <int DT>
-struct StepRegs {
-    static constexpr int VE = Traits<DT>::VE;
-    static constexpr int KPT = U * VE;
-    u32x4 v[U];
-};
+// One streaming step: each thread loads U 16-byte vectors, NT vectors apart.
+// `vb` points at the unit's first body vector; vector indices are relative to
+// it (a unit spans at most 2^31 vectors).
+// A unit's body vectors are read through a buffer resource: base in scalar
+// registers, a per-thread constant offset plus a wave-uniform step offset, and
+// the hardware range check returns zeros past the end (nvec * 16 bytes).  So
+// every load of a step is issued unconditionally, with no address arithmetic
+// per vector, and the code stays straight-line, which lets the compiler's
+// wait counts keep one step's loads in flight while the previous step is
+// filtered.  (Rows are below 2^31 bytes, so 32-bit offsets suffice.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t body_rsrc(const void* base, uint32_t bytes) {
+    // word 3: the raw-buffer format used for untyped loads on gfx9 parts
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
 
-template <int DT>
-__device__ __forceinline__ void load_step(StepRegs<DT>& R, const u32x4* vbase, int64_t v_begin,
-                                          int64_t v_end) {
+// Loads one streaming step: vector first + u*NT + threadIdx.x into R[u]
+// (zeros past the end).
+template <int U>
+__device__ __forceinline__ void load_step(u32x4 (&R)[U], __amdgpu_buffer_rsrc_t rs,
+                                          uint32_t first) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t v = v_begin + (int64_t)u * NT + threadIdx.x;
-        if (v < v_end) R.v[u] = gload(vbase + v);
-    }
+    for (int u = 0; u < U; ++u)
+        R[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             rs, (int)(threadIdx.x * 16u),
+                                             (int)((first + (uint32_t)u * NT) * 16u), 0));
 }
 
 // element e (0..VE-1) of a 16-byte vector, as raw bits
@@ -161,103 +175,392 @@ __device__ __forceinline__ uint32_t vec_elem(const u32x4& q, int e) {
 }
 
 // ---------------------------------------------------------------------------
-// logical candidate buffer: slots [0, lds_cap) in LDS, [lds_cap, gcap) in the
-// unit's workspace region
+// candidate buffers of one unit
+//   upper rung (keys >= T2): slots [0, lds_cap) in LDS, [lds_cap, hi_cap) in
+//                            the unit's workspace region;
+//   lower rung (T <= key < T2): slots [0, lo_cap) at region + HI_SLOTS.
 // ---------------------------------------------------------------------------
 
 struct Buf {
     uint32_t* gkey;
     uint32_t* gidx;
-    uint32_t lds_cap;
-    uint32_t gcap;
+    uint32_t lds_cap, hi_cap, lo_cap;
 };
 
-// every lane of the wave calls this together
-__device__ __forceinline__ void buf_append(Smem& sm, const Buf& B, bool pass, uint32_t key,
-                                           uint32_t col) {
-    uint64_t m;
-    const uint32_t pos = wave_ticket(&sm.cand_n, pass, m);
-    if (pass) {
-        if (pos < B.lds_cap) {
-            sm.key[pos] = key;
-            sm.idx[pos] = col;
-        } else if (pos < B.gcap) {
-            gstore(B.gkey + pos, key);
-            gstore(B.gidx + pos, col);
-        }
+__device__ __forceinline__ void put_hi(Smem& sm, const Buf& B, uint32_t pos, uint32_t key,
+                                       uint32_t col) {
+    if (pos < B.lds_cap) {
+        sm.key[pos] = key;
+        sm.idx[pos] = col;
+    } else if (pos < B.hi_cap) {
+        gstore_at(B.gkey, pos, key);
+        gstore_at(B.gidx, pos, col);
+    }
+}
+
+__device__ __forceinline__ void put_lo(const Buf& B, uint32_t pos, uint32_t key, uint32_t col) {
+    if (pos < B.lo_cap) {
+        gstore_at(B.gkey, HI_SLOTS + pos, key);
+        gstore_at(B.gidx, HI_SLOTS + pos, col);
     }
 }
 
 // ---------------------------------------------------------------------------
-// sampled threshold
+// sampled rungs
 // ---------------------------------------------------------------------------
 
-// Key T such that every workgroup of the row keeps keys >= T.  Rows with at
-// most SAMPLE columns are read whole and T is their exact k-th largest key.
-// Longer rows read SAMPLE_BLOCKS blocks of SAMPLE_BLOCK columns spread evenly
-// over [0, n); T is the sample's q-th largest key with
-//   q = ceil(mu + sigma * sqrt(mu) + 4),  mu = k * SAMPLE / n,
-// mu being the expected number of sampled keys above the row's k-th largest.
+struct Rungs {
+    uint32_t T;   // safe rung
+    uint32_t T2;  // likely rung, T2 >= T
+};
+
+// Rows with at most SAMPLE columns are read whole and T = T2 is a lower bound
+// of their k-th largest key.  Longer rows read SAMPLE_BLOCKS blocks of
+// SAMPLE_BLOCK columns spread evenly over [0, n); with mu = k * SAMPLE / n, the
+// expected number of sampled keys above the row's k-th largest,
+//   T  = the sample's q-th largest key,  q  = ceil(mu + sigma  * sqrt(mu) + 4),
+//   T2 = the sample's q2-th largest key, q2 = ceil(mu + sigma2 * sqrt(mu) + 1).
+// Keys are resolved to their top 19 bits for fp32 (a lower bound: every key
+// sharing the prefix passes, equal keys included) and exactly for 16-bit keys.
+// The loads are issued by sample_load; sample_rungs consumes them.
+struct Sample {
+    uint32_t key[SPT];  // raw bits until sample_rungs turns them into keys
+    uint32_t vmask;     // bit j: key[j] is a sampled key
+};
+
 template <int DT>
-__device__ __forceinline__ uint32_t sample_threshold(Smem& sm, const Params& p,
-                                     const typename Traits<DT>::raw_t* row, int64_t n) {
-    uint32_t keys[SPT];
-    uint32_t vmask = 0;
-    uint32_t q;
-    if (n <= SAMPLE) {
+__device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* row, int64_t n,
+                                            Sample& S) {
+    // one straight run of loads for both cases (positions clamped, so all are
+    // in flight at once); short rows mask out positions >= n
+    const bool whole = n <= SAMPLE;
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    S.vmask = 0;
 #pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int64_t pos = threadIdx.x + (int64_t)j * NT;
-            keys[j] = 0;
-            if (pos < n) {
-                keys[j] = to_key<DT>(gload(row + pos));
-                vmask |= 1u << j;
-            }
-        }
-        q = (uint32_t)p.k;
-    } else {
-        const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int64_t b = w + j * WAVES;
-            const int64_t start = b * (n - SAMPLE_BLOCK) / (SAMPLE_BLOCKS - 1);
-            keys[j] = to_key<DT>(gload(row + start + lane));
-        }
-        vmask = (SPT >= 32) ? 0xFFFFFFFFu : ((1u << SPT) - 1u);
-        const float mu = (float)p.k * (float)SAMPLE / (float)n;
-        const float qf = ceilf(mu + p.sigma * sqrtf(mu) + 4.0f);
-        q = qf >= (float)SAMPLE ? (uint32_t)SAMPLE : (uint32_t)qf;
+    for (int j = 0; j < SPT; ++j) {
+        const int64_t b = w + j * WAVES;
+        const int64_t pw = threadIdx.x + (int64_t)j * NT;
+        const int64_t pos = whole ? (pw < n ? pw : n - 1)
+                                  : b * (n - SAMPLE_BLOCK) / (SAMPLE_BLOCKS - 1) + lane;
+        S.key[j] = gload(row + pos);
+        if (!whole || pw < n) S.vmask |= 1u << j;
     }
-    uint32_t T, gt;
-    block_select<Traits<DT>::BITS>(
-        sm,
-        [&](auto f) {
+}
+
+template <int DT>
+__device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t n, Sample& S) {
+    constexpr int BITS = Traits<DT>::BITS;
+    uint32_t q = (uint32_t)p.k, q2 = q;
+    if (n > SAMPLE) {
+        const float mu = (float)p.k * (float)SAMPLE / (float)n;
+        const float sq = sqrtf(mu);
+        const float qf = ceilf(mu + p.sigma * sq + 4.0f);
+        const float q2f = ceilf(mu + p.sigma2 * sq + 1.0f);
+        q = qf >= (float)SAMPLE ? (uint32_t)SAMPLE : (uint32_t)qf;
+        q2 = q2f >= (float)q ? q : (uint32_t)q2f;
+    }
 #pragma unroll
-            for (int j = 0; j < SPT; ++j)
-                if ((vmask >> j) & 1u) f(keys[j]);
-        },
-        q, T, gt);
-    return T;
+    for (int j = 0; j < SPT; ++j) S.key[j] = to_key<DT>((typename Traits<DT>::raw_t)S.key[j]);
+    auto visit = [&](auto f) {
+#pragma unroll
+        for (int j = 0; j < SPT; ++j)
+            if ((S.vmask >> j) & 1u) f(S.key[j]);
+    };
+    Rungs R;
+    block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(sm, visit, q, q2, R.T, R.T2);
+    return R;
 }
 
 // ---------------------------------------------------------------------------
 // fast filter: one pass, no barriers inside the loop
 // ---------------------------------------------------------------------------
 
+// Rung tests on an element's raw bits.  With FAST (both rungs >= +0, the
+// normal case) "key >= T" is a signed compare of the raw bits with the
+// rung's raw bits: non-negative values order like their bits and negative
+// ones are negative integers.  Otherwise the order-preserving key is formed.
+template <int DT, bool FAST>
+struct RungTest {
+    int32_t a, a2;  // FAST: the rungs' raw bits, sign-extended
+    uint32_t t, t2; // otherwise: the rungs as keys
+    __device__ __forceinline__ explicit RungTest(const Rungs& G) {
+        if constexpr (Traits<DT>::BITS == 32) {
+            a = (int32_t)(G.T & 0x7FFFFFFFu);
+            a2 = (int32_t)(G.T2 & 0x7FFFFFFFu);
+        } else {
+            a = (int32_t)(G.T & 0x7FFFu);
+            a2 = (int32_t)(G.T2 & 0x7FFFu);
+        }
+        t = G.T;
+        t2 = G.T2;
+    }
+    // element e of vector q: *in = key >= T, *up = key >= T2
+    __device__ __forceinline__ void operator()(const u32x4& q, int e, bool& in, bool& up) const {
+        if constexpr (FAST) {
+            int32_t v;
+            if constexpr (Traits<DT>::BITS == 32) {
+                v = (int32_t)q[e];
+            } else {
+                const uint32_t w = q[e >> 1];
+                v = (e & 1) ? ((int32_t)w >> 16) : (int32_t)(int16_t)(w & 0xFFFFu);
+            }
+            in = v >= a;
+            up = v >= a2;
+        } else {
+            const uint32_t key = to_key<DT>(vec_elem<DT>(q, e));
+            in = key >= t;
+            up = key >= t2;
+        }
+    }
+};
+
+// Raw bits that fail every raw-bit rung test (a negative integer in both
+// halves for 16-bit elements); a partial last step is padded with them.
 template <int DT>
-__device__ __forceinline__ void filter_step(Smem& sm, const Buf& B, const StepRegs<DT>& R,
-                                            int64_t v_begin, int64_t v_end, int64_t h,
-                                            uint32_t T) {
+__device__ __forceinline__ constexpr uint32_t fail_word() {
+    return Traits<DT>::BITS == 32 ? 0x80000000u : 0x80008000u;
+}
+
+// key of element e of q when the element is known to be >= +0
+template <int DT>
+__device__ __forceinline__ uint32_t nonneg_key(const u32x4& q, int e) {
+    if constexpr (Traits<DT>::BITS == 32) {
+        return q[e] | 0x80000000u;
+    } else {
+        const uint32_t w = q[e >> 1];
+        return ((e & 1) ? (w >> 16) : (w & 0xFFFFu)) | 0x8000u;
+    }
+}
+
+// Filters one streaming step in two passes over the thread's U vectors.
+// Pass 1 counts: each compare yields a 64-lane mask (ballot), so the wave's
+// upper- and lower-rung totals are scalar popcounts; one LDS ticket per rung
+// then reserves the wave's slots.  Pass 2 repeats the compares and, only for
+// elements whose mask is non-empty, writes each candidate at the ticket base
+// plus its rank among the wave's lanes (mbcnt).  With FAST every vector of
+// the step is valid (a partial step has been padded with fail_word).
+template <int DT, bool FAST>
+__device__ __forceinline__ void filter_step(Smem& sm, const Buf& B,
+                                            u32x4 (&R)[Traits<DT>::U], uint32_t first,
+                                            uint32_t nvec, uint32_t col0,
+                                            const RungTest<DT, FAST>& test) {
     constexpr int VE = Traits<DT>::VE;
+    constexpr int U = Traits<DT>::U;
+    uint32_t th = 0, ti = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t v = v_begin + (int64_t)u * NT + threadIdx.x;
-        const bool ok = v < v_end;
+        const bool ok = FAST || first + (uint32_t)u * NT + threadIdx.x < nvec;
 #pragma unroll
         for (int e = 0; e < VE; ++e) {
-            const uint32_t key = to_key<DT>(vec_elem<DT>(R.v[u], e));
-            buf_append(sm, B, ok && key >= T, key, (uint32_t)(h + v * VE + e));
+            bool in, up;
+            test(R[u], e, in, up);
+            uint64_t mi = ballot(in), mh = ballot(up);
+            if constexpr (!FAST) {
+                const uint64_t okm = ballot(ok);
+                mi &= okm;
+                mh &= okm;
+            }
+            ti += (uint32_t)__popcll(mi);  // T2 >= T: the upper keys are among them
+            th += (uint32_t)__popcll(mh);
         }
+    }
+    if (ti == 0) return;  // uniform
+    const uint32_t tl = ti - th;
+    uint32_t bh = 0, bl = 0;
+    if (lane_id() == 0) {
+        if (th) bh = atomicAdd(&sm.cand_n, th);
+        if (tl) bl = atomicAdd(&sm.lo_n, tl);
+    }
+    bh = first_lane_value(bh);
+    bl = first_lane_value(bl);
+    // the compares are redone below rather than kept: holding every mask of
+    // the first pass would take more scalar registers than there are
+#pragma unroll
+    for (int u = 0; u < U; ++u) __asm__ volatile("" : "+v"(R[u]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const uint32_t v = first + (uint32_t)u * NT + threadIdx.x;
+        const bool ok = FAST || v < nvec;
+        const uint32_t colu = col0 + v * VE;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            bool in, up;
+            test(R[u], e, in, up);
+            const bool h = ok && up, l = ok && in && !up;
+            uint64_t mi = ballot(in);
+            if constexpr (!FAST) mi &= ballot(ok);
+            if (mi == 0) continue;  // uniform
+            const uint64_t mh = ballot(h), ml = mi & ~mh;
+            const uint32_t key = FAST ? nonneg_key<DT>(R[u], e) : to_key<DT>(vec_elem<DT>(R[u], e));
+            const uint32_t col = colu + (uint32_t)e;
+            if (mh) {
+                const uint32_t nh = (uint32_t)__popcll(mh);
+                if (bh + nh <= B.lds_cap) {  // uniform: the usual case
+                    if (h) {
+                        const uint32_t pos = bh + mbcnt(mh);
+                        sm.key[pos] = key;
+                        sm.idx[pos] = col;
+                    }
+                } else if (h) {
+                    put_hi(sm, B, bh + mbcnt(mh), key, col);
+                }
+                bh += nh;
+            }
+            if (ml) {
+                if (l) put_lo(B, bl + mbcnt(ml), key, col);
+                bl += (uint32_t)__popcll(ml);
+            }
+        }
+    }
+}
+
+// Pads the vectors of a partial step that lie past the unit's end.
+template <int DT>
+__device__ __forceinline__ void pad_step(u32x4 (&R)[Traits<DT>::U], uint32_t first,
+                                         uint32_t nvec) {
+    constexpr uint32_t F = fail_word<DT>();
+#pragma unroll
+    for (int u = 0; u < Traits<DT>::U; ++u)
+        if (first + (uint32_t)u * NT + threadIdx.x >= nvec) R[u] = u32x4{F, F, F, F};
+}
+
+// Largest element of a vector as a signed integer of its raw bits: the
+// raw-bit rung test passes for some element exactly when it passes for this.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ __forceinline__ int32_t vec_max_raw(const u32x4& q) {
+    if constexpr (Traits<DT>::BITS == 32) {
+        const int32_t a = (int32_t)q[0] > (int32_t)q[1] ? (int32_t)q[0] : (int32_t)q[1];
+        const int32_t b = (int32_t)q[2] > (int32_t)q[3] ? (int32_t)q[2] : (int32_t)q[3];
+        return a > b ? a : b;
+    } else {
+        // (each word copied out first: a bit cast of a vector element
+        // expression is not reliable with this compiler)
+        const uint32_t w0 = q[0], w1 = q[1], w2 = q[2], w3 = q[3];
+        const s16x2 m = __builtin_elementwise_max(
+            __builtin_elementwise_max(__builtin_bit_cast(s16x2, w0), __builtin_bit_cast(s16x2, w1)),
+            __builtin_elementwise_max(__builtin_bit_cast(s16x2, w2), __builtin_bit_cast(s16x2, w3)));
+        return m.x > m.y ? (int32_t)m.x : (int32_t)m.y;
+    }
+}
+
+// Drains a wave's staging queue (slots [0, sc), sc <= STAGE, wave-uniform):
+// in rounds of 64, lane l takes slot l of the round and runs the element
+// filter on its vector; the candidates get LDS tickets as in filter_step.
+// Every lane of the wave calls it; no barrier (the queue is the wave's own).
+template <int DT>
+__device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col0,
+                                            const RungTest<DT, true>& test, uint32_t sc) {
+    constexpr int VE = Traits<DT>::VE;
+    constexpr uint32_t F = fail_word<DT>();
+    const uint32_t base = (threadIdx.x >> 6) * STAGE;
+    const uint32_t l = lane_id();
+    for (uint32_t r0 = 0; r0 < sc; r0 += 64) {
+        const uint32_t i = r0 + l;
+        u32x4 q = u32x4{F, F, F, F};
+        uint32_t v = 0;
+        if (i < sc) {
+            q = sm.stage.vec[base + i];
+            v = sm.stage.v[base + i];
+        }
+        uint32_t th = 0, ti = 0;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            bool in, up;
+            test(q, e, in, up);
+            ti += (uint32_t)__popcll(ballot(in));
+            th += (uint32_t)__popcll(ballot(up));
+        }
+        const uint32_t tl = ti - th;  // ti > 0: a staged vector holds a candidate
+        uint32_t bh = 0, bl = 0;
+        if (l == 0) {
+            if (th) bh = atomicAdd(&sm.cand_n, th);
+            if (tl) bl = atomicAdd(&sm.lo_n, tl);
+        }
+        bh = first_lane_value(bh);
+        bl = first_lane_value(bl);
+        const uint32_t colv = col0 + v * VE;
+#pragma unroll
+        for (int e = 0; e < VE; ++e) {
+            bool in, up;
+            test(q, e, in, up);
+            const uint64_t mi = ballot(in);
+            if (mi == 0) continue;  // uniform
+            const uint64_t mh = ballot(up), ml = mi & ~mh;
+            const uint32_t key = nonneg_key<DT>(q, e);
+            const uint32_t col = colv + (uint32_t)e;
+            if (up) put_hi(sm, B, bh + mbcnt(mh), key, col);
+            if (in && !up) put_lo(B, bl + mbcnt(ml), key, col);
+            bh += (uint32_t)__popcll(mh);
+            bl += (uint32_t)__popcll(ml);
+        }
+    }
+}
+
+// One streaming step with both rungs >= +0.  Per vector: the largest raw
+// element against the lower rung; the (few) vectors holding a candidate are
+// appended to the wave's staging queue in LDS (ballot + mbcnt positions), and
+// the queue is drained once it holds STAGE_DRAIN vectors, which keeps it below
+// STAGE_DRAIN + 64 <= STAGE.  The per-element work then runs on full rounds
+// of staged vectors instead of on every element of the step.
+template <int DT>
+__device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (&R)[Traits<DT>::U],
+                                           uint32_t first, uint32_t col0,
+                                           const RungTest<DT, true>& test, uint32_t& sc) {
+    static_assert(STAGE_DRAIN + 64 <= STAGE, "staging queue bound");
+    const uint32_t base = (threadIdx.x >> 6) * STAGE;
+#pragma unroll
+    for (int u = 0; u < Traits<DT>::U; ++u) {
+        const bool hit = vec_max_raw<DT>(R[u]) >= test.a;
+        const uint64_t m = ballot(hit);
+        if (m == 0) continue;  // uniform
+        if (hit) {
+            const uint32_t pos = base + sc + mbcnt(m);
+            sm.stage.vec[pos] = R[u];
+            sm.stage.v[pos] = first + (uint32_t)u * NT + threadIdx.x;
+        }
+        sc += (uint32_t)__popcll(m);
+        if (sc >= (uint32_t)STAGE_DRAIN) {
+            drain_stage<DT>(sm, B, col0, test, sc);
+            sc = 0;
+        }
+    }
+}
+
+// The streaming loop over a unit's body vectors, starting with step 0 already
+// in RA (or in flight to it): two register sets in turn, the next step's loads
+// are in flight while the current one is filtered.  FAST (both rungs >= +0)
+// uses the staged vector filter, otherwise the element filter.
+template <int DT, bool FAST>
+__device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[Traits<DT>::U],
+                                            u32x4 (&RB)[Traits<DT>::U],
+                                            __amdgpu_buffer_rsrc_t rs, uint32_t nvec,
+                                            uint32_t col0, const Rungs& G) {
+    constexpr uint32_t STEP = (uint32_t)NT * Traits<DT>::U;
+    const RungTest<DT, FAST> test(G);
+    uint32_t sc = 0;  // staged vectors of this wave (FAST)
+    auto step = [&](u32x4 (&R)[Traits<DT>::U], uint32_t vs) {
+        if constexpr (FAST) {
+            if (vs + STEP > nvec) pad_step<DT>(R, vs, nvec);
+            stage_step<DT>(sm, B, R, vs, col0, test, sc);
+        } else {
+            filter_step<DT, false>(sm, B, R, vs, nvec, col0, test);
+        }
+    };
+    // Step 0 is filtered before the loop, so on entry and on the back edge
+    // alike exactly the loads of RB are in flight at the loop header: the
+    // compiler's wait counts then let them stay in flight while RA is filtered.
+    load_step(RB, rs, STEP);
+    step(RA, 0);
+    for (uint32_t vs = STEP; vs < nvec; vs += 2 * STEP) {
+        load_step(RA, rs, vs + STEP);
+        step(RB, vs);
+        if (vs + STEP >= nvec) break;
+        load_step(RB, rs, vs + 2 * STEP);
+        step(RA, vs + STEP);
+    }
+    if constexpr (FAST) {
+        if (sc) drain_stage<DT>(sm, B, col0, test, sc);
     }
 }
 
@@ -265,12 +568,17 @@ __device__ __forceinline__ void filter_step(Smem& sm, const Buf& B, const StepRe
 template <int DT>
 __device__ __forceinline__ void filter_scalars(Smem& sm, const Buf& B,
                                                const typename Traits<DT>::raw_t* row, int64_t a,
-                                               int64_t b, uint32_t T) {
+                                               int64_t b, const Rungs& G) {
     for (int64_t base = a; base < b; base += NT) {
         const int64_t c = base + threadIdx.x;
         const bool ok = c < b;
         const uint32_t key = ok ? to_key<DT>(gload(row + c)) : 0u;
-        buf_append(sm, B, ok && key >= T, key, (uint32_t)c);
+        const bool hi = ok && key >= G.T2;
+        const bool lo = ok && !hi && key >= G.T;
+        const uint32_t ph = wave_ticket_n(&sm.cand_n, hi ? 1u : 0u);
+        const uint32_t pl = wave_ticket_n(&sm.lo_n, lo ? 1u : 0u);
+        if (hi) put_hi(sm, B, ph, key, (uint32_t)c);
+        if (lo) put_lo(B, pl, key, (uint32_t)c);
     }
 }
 
@@ -291,7 +599,7 @@ template <int DT, int KPT>
 __device__ __forceinline__ void compact(Smem& sm, int k, const uint32_t (&kk)[KPT], const uint32_t (&cc)[KPT],
                         uint32_t vm, Thr& thr, uint32_t old_n) {
     uint32_t K, gt;
-    block_select<Traits<DT>::BITS>(
+    block_select_exact(
         sm,
         [&](auto f) {
             for (uint32_t q = threadIdx.x; q < old_n; q += NT) f(sm.key[q]);
@@ -411,6 +719,27 @@ __device__ __forceinline__ void careful_filter(Smem& sm, const Params& p, const 
     }
 }
 
+// Adds the workspace entries gk[0, m) / gi[0, m) (all passing thr) to the LDS
+// candidates [0, sm.cand_n) with the compaction filter, E entries per thread per
+// round: all loads of a round are issued before any is used.
+template <int DT>
+__device__ __forceinline__ void ingest_global(Smem& sm, int k, const uint32_t* gk,
+                                              const uint32_t* gi, uint32_t m, Thr& thr) {
+    constexpr int E = 8;
+    for (uint32_t b = 0; b < m; b += (uint32_t)NT * E) {
+        uint32_t kk[E], cc[E], vm = 0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint32_t q = b + (uint32_t)e * NT + threadIdx.x;
+            const uint32_t qc = q < m ? q : m - 1;
+            kk[e] = gload(gk + qc);
+            cc[e] = gload(gi + qc);
+            if (q < m) vm |= 1u << e;
+        }
+        careful_step<DT, E>(sm, k, kk, cc, vm, thr);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // final selection and epilogue
 // ---------------------------------------------------------------------------
@@ -428,51 +757,12 @@ struct LdsSrc {
     }
 };
 
-struct BufSrc {  // logical buffer: LDS slots [0, lds_n), workspace slots [lds_cap, n)
-    uint32_t n, lds_cap;
-    const uint32_t* gkey;
-    const uint32_t* gidx;
-    template <class F>
-    __device__ __forceinline__ void for_each(Smem& sm, F f) const {
-        const uint32_t nl = n < lds_cap ? n : lds_cap;
-        for (uint32_t b = 0; b < nl; b += NT) {
-            const uint32_t q = b + threadIdx.x;
-            const bool ok = q < nl;
-            f(ok, ok ? sm.key[q] : 0u, ok ? sm.idx[q] : 0u);
-        }
-        for (uint32_t b = lds_cap; b < n; b += NT) {
-            const uint32_t q = b + threadIdx.x;
-            const bool ok = q < n;
-            f(ok, ok ? gload(gkey + q) : 0u, ok ? gload(gidx + q) : 0u);
-        }
-    }
-};
-
-struct SegSrc {  // the workspace regions of a split row's units
-    int nseg;
-    const uint32_t* gkey;  // region of unit 0 of the row
-    const uint32_t* gidx;
-    template <class F>
-    __device__ __forceinline__ void for_each(Smem& sm, F f) const {
-        for (int s = 0; s < nseg; ++s) {
-            const uint32_t n = sm.seg_cnt[s];
-            const uint32_t* kp = gkey + (size_t)s * WSCAP;
-            const uint32_t* ip = gidx + (size_t)s * WSCAP;
-            for (uint32_t b = 0; b < n; b += NT) {
-                const uint32_t q = b + threadIdx.x;
-                const bool ok = q < n;
-                f(ok, ok ? gload(kp + q) : 0u, ok ? gload(ip + q) : 0u);
-            }
-        }
-    }
-};
-
 // Selects the top k of `src` (which must hold at least k entries and contain
 // a top-k of the row) and writes them through the policy.
 template <int DT, class Policy, class Src>
 __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r, int64_t base, const Src& src) {
     uint32_t K, gt;
-    block_select<Traits<DT>::BITS>(
+    block_select_exact(
         sm,
         [&](auto f) {
             src.for_each(sm, [&](bool ok, uint32_t key, uint32_t) {
@@ -553,108 +843,166 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const Slice s = make_slice<DT>(row, n, c, eff);
     uint32_t* gkey = p.ws_key + (size_t)unit * WSCAP;
     uint32_t* gidx = p.ws_idx + (size_t)unit * WSCAP;
-    const Buf B{gkey, gidx, (uint32_t)p.lds_cap, (uint32_t)p.wscap};
-    const u32x4* vb = reinterpret_cast<const u32x4*>(row + s.h);
-    const int64_t step = (int64_t)NT * U;
+    const Buf B{gkey, gidx, (uint32_t)p.lds_cap, (uint32_t)p.hi_cap, (uint32_t)p.lo_cap};
+    // body vectors of this unit, relative indexing (32-bit)
+    const u32x4* vb = reinterpret_cast<const u32x4*>(row + s.h) + s.v0;
+    const uint32_t nvec = (uint32_t)(s.v1 - s.v0);
+    const uint32_t col0 = (uint32_t)(s.h + s.v0 * Traits<DT>::VE);
+    constexpr int U = Traits<DT>::U;
 
-    // first streaming step is issued before the threshold is known
-    StepRegs<DT> cur;
-    if (p.force_path != FORCE_CAREFUL) load_step<DT>(cur, vb, s.v0, s.v1);
-    if (threadIdx.x == 0) sm.cand_n = 0;
-    const uint32_t T = sample_threshold<DT>(sm, p, row, n);
-
-    bool in_lds_only = false;
-    if (p.force_path != FORCE_CAREFUL) {
-        filter_scalars<DT>(sm, B, row, s.s0, s.s1, T);
-        for (int64_t vs = s.v0; vs < s.v1; vs += step) {
-            StepRegs<DT> nxt;
-            if (vs + step < s.v1) load_step<DT>(nxt, vb, vs + step, s.v1);
-            filter_step<DT>(sm, B, cur, vs, s.v1, s.h, T);
-            cur = nxt;
-        }
-        filter_scalars<DT>(sm, B, row, s.t0, s.t1, T);
-        __syncthreads();
-        const uint32_t filled = sm.cand_n;
-        __syncthreads();  // everyone has read the count before it can change
-        if (filled > B.gcap) {  // overflow: re-filter this unit with compaction
-            if (threadIdx.x == 0) gatomic_add(p.ws_stats + 0, 1u);
-            careful_filter<DT>(sm, p, row, s, Thr{T, false});
-            in_lds_only = true;
-        }
-    } else {
-        careful_filter<DT>(sm, p, row, s, Thr{T, false});
-        in_lds_only = true;
+    // The sample's loads go out first, then the first streaming step's, which
+    // stays in flight while the rungs are computed.
+    Sample S;
+    sample_load<DT>(row, n, S);
+    u32x4 RA[U], RB[U];
+    bool refiltered = p.force_path == FORCE_CAREFUL;
+    // (always issued, also where the careful filter will ignore it: straight-line
+    // code keeps the wait counts exact)
+    const __amdgpu_buffer_rsrc_t rs = body_rsrc(vb, nvec * 16u);
+    load_step(RA, rs, 0u);
+    if (threadIdx.x == 0) {
+        sm.cand_n = 0;
+        sm.lo_n = 0;
     }
-    __syncthreads();
-    const uint32_t cand = sm.cand_n;
-    __syncthreads();
-    const uint32_t lcap = in_lds_only ? (uint32_t)CAP : B.lds_cap;
+    hist_clear(sm);  // every select leaves the histogram zeroed again
+    lds_sync();      // the loads stay in flight
+    const Rungs G = sample_rungs<DT>(sm, p, n, S);
+
+    uint32_t nh, nl, lcap;  // upper / lower candidates, on-chip part of the upper ones
+    if (!refiltered) {
+        filter_scalars<DT>(sm, B, row, s.s0, s.s1, G);
+        constexpr uint32_t SIGN = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
+        if (nvec == 0) {
+        } else if (G.T & G.T2 & SIGN) {  // both rungs >= +0: raw-bit compares
+            stream_unit<DT, true>(sm, B, RA, RB, rs, nvec, col0, G);
+        } else {
+            stream_unit<DT, false>(sm, B, RA, RB, rs, nvec, col0, G);
+        }
+        filter_scalars<DT>(sm, B, row, s.t0, s.t1, G);
+        __syncthreads();  // also completes the workspace stores of every thread
+        nh = sm.cand_n;
+        nl = sm.lo_n;
+        hist_clear(sm);  // the staging queues overlaid the histogram
+        lds_sync();      // everyone has read the counts before they can change
+        if (nh > B.hi_cap || nl > B.lo_cap) {  // slots ran out: re-filter with compaction
+            if (threadIdx.x == 0) gatomic_add(p.ws_stats + 0, 1u);
+            refiltered = true;
+        }
+    }
+    if (refiltered) {
+        careful_filter<DT>(sm, p, row, s, Thr{G.T, false});
+        __syncthreads();
+        nh = sm.cand_n;  // every candidate is on chip now
+        nl = 0;
+        __syncthreads();
+    }
+    lcap = refiltered ? (uint32_t)CAP : B.lds_cap;
+    const uint32_t own = nh < lcap ? nh : lcap;
 
     if (eff == 1) {
-        if (cand < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
-            if (threadIdx.x == 0 && cand < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
+        if (nh + nl < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
+            if (threadIdx.x == 0 && nh + nl < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
             __syncthreads();
             whole_row<DT, Policy>(sm, p, r, base, n, row);
             return;
         }
-        select_and_emit<DT, Policy>(sm, p, r, base, BufSrc{cand, lcap, gkey, gidx});
+        const bool need_lo = nh < (uint32_t)p.k;
+        if (nh > own || need_lo) {  // pull spilled / lower-rung candidates into LDS
+            if (threadIdx.x == 0) {
+                sm.cand_n = own;
+                if (nh > own) gatomic_add(p.ws_stats + 2, 1u);
+                if (need_lo) gatomic_add(p.ws_stats + 3, 1u);
+            }
+            __syncthreads();
+            Thr thr{G.T, false};
+            if (nh > own) ingest_global<DT>(sm, p.k, gkey + own, gidx + own, nh - own, thr);
+            if (need_lo)
+                ingest_global<DT>(sm, p.k, gkey + HI_SLOTS, gidx + HI_SLOTS, nl, thr);
+        }
+        __syncthreads();
+        const uint32_t m = sm.cand_n;
+        __syncthreads();
+        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc{m});
         return;
     }
 
-    // split row: publish this unit's candidates, then take a ticket
-    {
-        const uint32_t nl = cand < lcap ? cand : lcap;
-        for (uint32_t q = threadIdx.x; q < nl; q += NT) {
-            gstore(gkey + q, sm.key[q]);
-            gstore(gidx + q, sm.idx[q]);
-        }
-        if (threadIdx.x == 0) gstore(p.ws_count + unit, cand);
+    // split row: publish this unit's on-chip candidates, then take a ticket
+    for (uint32_t q = threadIdx.x; q < own; q += NT) {
+        gstore(gkey + q, sm.key[q]);
+        gstore(gidx + q, sm.idx[q]);
     }
-    // release: every thread's candidate stores, then the ticket (agent scope)
-    __threadfence();
+    if (threadIdx.x == 0) {
+        // a re-filtered unit keeps every key >= T (or its chunk's top k) on the
+        // upper list without separating the rungs: the flag makes the merge
+        // read every lower list too
+        gstore(p.ws_count + unit, nh);
+        gstore(p.ws_count_lo + unit, nl | (refiltered ? 0x80000000u : 0u));
+    }
+    // Hand-off: the barrier orders every thread's candidate stores before
+    // thread 0's agent-scope release fence, which precedes the ticket; the
+    // unit that takes the last ticket issues an agent-scope acquire fence
+    // before the barrier that releases its other threads to read.  One fence
+    // per workgroup: each one writes back or invalidates the whole L2.
     __syncthreads();
     if (threadIdx.x == 0) {
-        __threadfence();
-        const uint32_t old = __hip_atomic_fetch_add((VTS_GLOBAL uint32_t*)(p.ws_ticket + r), 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        sm.flag = (old == (uint32_t)eff - 1u) ? 1u : 0u;
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t old = __hip_atomic_fetch_add((VTS_GLOBAL uint32_t*)(p.ws_ticket + r), 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (uint32_t)eff - 1u;
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        sm.flag = last ? 1u : 0u;
     }
     __syncthreads();
     if (sm.flag == 0) return;
-    __threadfence();  // acquire side for every thread of the merging workgroup
 
     // last unit of the row: merge
     const uint32_t unit0 = (uint32_t)r * (uint32_t)p.nsplit;
-    if (threadIdx.x < (unsigned)eff) sm.seg_cnt[threadIdx.x] = gload(p.ws_count + unit0 + threadIdx.x);
+    if (threadIdx.x < (unsigned)eff) {
+        sm.seg_hi[threadIdx.x] = gload(p.ws_count + unit0 + threadIdx.x);
+        sm.seg_lo[threadIdx.x] = gload(p.ws_count_lo + unit0 + threadIdx.x);
+    }
     if (threadIdx.x == 0) gstore(p.ws_ticket + r, 0u);  // self-restoring
     __syncthreads();
-    uint32_t total = 0;
-    for (int q = 0; q < eff; ++q) total += sm.seg_cnt[q];
-    const uint32_t* rkey = p.ws_key + (size_t)unit0 * WSCAP;
-    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * WSCAP;
-    if (total < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
-        if (threadIdx.x == 0 && total < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
+    uint32_t th = 0, tl = 0;
+    bool mixed = false;  // some unit was re-filtered
+    for (int q = 0; q < eff; ++q) {
+        th += sm.seg_hi[q];
+        tl += sm.seg_lo[q] & 0x7FFFFFFFu;
+        mixed |= (sm.seg_lo[q] >> 31) != 0;
+    }
+    if (th + tl < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
+        if (threadIdx.x == 0 && th + tl < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
         __syncthreads();
         whole_row<DT, Policy>(sm, p, r, base, n, row);
         return;
     }
-    if (total <= (uint32_t)p.lds_cap) {
-        uint32_t off = 0;
-        for (int q = 0; q < eff; ++q) {
-            const uint32_t m = sm.seg_cnt[q];
-            for (uint32_t i = threadIdx.x; i < m; i += NT) {
-                sm.key[off + i] = gload(rkey + (size_t)q * WSCAP + i);
-                sm.idx[off + i] = gload(ridx + (size_t)q * WSCAP + i);
-            }
-            off += m;
-        }
-        __syncthreads();
-        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc{total});
-    } else {
-        if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
-        select_and_emit<DT, Policy>(sm, p, r, base, SegSrc{eff, rkey, ridx});
+    const bool need_lo = th < (uint32_t)p.k || mixed;
+    // This unit's on-chip candidates stay in place; the other units' (and this
+    // unit's spilled ones) are pulled in with the compaction filter.
+    if (threadIdx.x == 0) {
+        sm.cand_n = own;
+        if (th > (uint32_t)CAP) gatomic_add(p.ws_stats + 2, 1u);
+        if (need_lo) gatomic_add(p.ws_stats + 3, 1u);
     }
+    __syncthreads();
+    const uint32_t* rkey = p.ws_key + (size_t)unit0 * WSCAP;
+    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * WSCAP;
+    Thr thr{G.T, false};
+    for (int q = 0; q < eff; ++q) {
+        const uint32_t mq = sm.seg_hi[q];
+        const uint32_t from = q == c ? own : 0u;
+        if (mq > from)
+            ingest_global<DT>(sm, p.k, rkey + (size_t)q * WSCAP + from,
+                              ridx + (size_t)q * WSCAP + from, mq - from, thr);
+        const uint32_t lq = sm.seg_lo[q] & 0x7FFFFFFFu;
+        if (need_lo && lq > 0)
+            ingest_global<DT>(sm, p.k, rkey + (size_t)q * WSCAP + HI_SLOTS,
+                              ridx + (size_t)q * WSCAP + HI_SLOTS, lq, thr);
+    }
+    __syncthreads();
+    const uint32_t m = sm.cand_n;
+    __syncthreads();
+    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc{m});
 }
 
 // ---------------------------------------------------------------------------
