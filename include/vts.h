@@ -90,10 +90,11 @@ int vts_workspace_init(void* workspace, size_t bytes, void* stream);
  * next_n      >= 1, must divide num_rows.
  * compress_ratio >= 1.
  * pre_idx     device int32[num_rows / next_n, top_k] or NULL: the previous
- *             step's selection for each request, used only to steer the
- *             threshold estimate (entries outside [0, n) are ignored).  Must be
- *             16-byte aligned; otherwise it is ignored and the call returns
- *             VTS_WARN_HINT_DISCARDED.  Results never depend on it.
+ *             step's selection for each request, which the pages allow as a
+ *             sampling anchor only.  It is validated (16-byte aligned, else
+ *             ignored with VTS_WARN_HINT_DISCARDED) and never read by the
+ *             current kernels, which estimate every threshold from a strided
+ *             sample of the row.  Results never depend on it.
  * out_indices device int32[num_rows, top_k], 16-byte aligned.  Row r receives
  *             the column indices of its top-k (in no particular order) when
  *             n > top_k; the indices 0..n-1 followed by -1 when n <= top_k (all

@@ -38,7 +38,9 @@
  *     ascending column so its own output is deterministic;
  *   - NaN: the pages call its order implementation specific.  The oracle puts a
  *     NaN with the sign bit clear above +inf and one with the sign bit set
- *     below -inf, so its comparison is a total order; no parity case holds NaN;
+ *     below -inf, so its comparison is a total order; no parity case holds NaN
+ *     and this order is parity unpinned (rows with NaN are checked for valid,
+ *     distinct indices only);
  *   - value padding: -FLT_MAX for fp32; for bf16/fp16 the lowest finite value
  *     of that type (0xFF7F, 0xFBFF);
  *   - transform row window: n = clamp(length, 0, width - row_start); a row
