@@ -188,7 +188,7 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *   VTS_TUNE_FORCE_PATH   0 normal, 1 every chunk uses the compaction filter,
  *                         2 every row is re-selected over the whole row
  *   VTS_TUNE_LDS_SLOTS    on-chip candidate slots before spilling to the
- *                         workspace (0 = default; 64..4096)
+ *                         workspace (0 = default; 64..3840)
  *   VTS_TUNE_SPILL_SLOTS  workspace candidate slots per workgroup and rung
  *                         before a chunk is re-filtered (0 = default; 64..8192)
  *   VTS_TUNE_SAMPLE_SIGMA margin of the safe threshold rung in tenths of a
@@ -196,7 +196,9 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *   VTS_TUNE_LIKELY_SIGMA margin of the likely rung, same unit (0 = 20; a
  *                         value >= the safe margin merges the two rungs)
  *   VTS_TUNE_MIN_CHUNK    valid columns per workgroup below which a row is not
- *                         split further (0 = default 16384; 256..2^20)
+ *                         split further (0 = default 32768; 256..2^20)
+ *   VTS_TUNE_NO_BALANCE   1 turns off the length-balanced placement of rows on
+ *                         compute units (0 = on where it applies)
  * The workspace size follows the split count in force when it is queried.
  * Returns VTS_OK or VTS_ERR_INVALID for an unknown key or value. */
 enum {
@@ -206,7 +208,8 @@ enum {
     VTS_TUNE_SPILL_SLOTS = 4,
     VTS_TUNE_SAMPLE_SIGMA = 5,
     VTS_TUNE_MIN_CHUNK = 6,
-    VTS_TUNE_LIKELY_SIGMA = 7
+    VTS_TUNE_LIKELY_SIGMA = 7,
+    VTS_TUNE_NO_BALANCE = 8
 };
 int vts_set_tuning(int32_t key, int64_t value);
 

@@ -37,7 +37,8 @@ def to_device_scores(x_bits: np.ndarray, dtype: int, width: int, offset: int = 0
 def tuning(**kw):
     keys = dict(nsplit=vts.TUNE_NSPLIT, force=vts.TUNE_FORCE_PATH, lds=vts.TUNE_LDS_SLOTS,
                 spill=vts.TUNE_SPILL_SLOTS, sigma=vts.TUNE_SAMPLE_SIGMA,
-                min_chunk=vts.TUNE_MIN_CHUNK, likely=vts.TUNE_LIKELY_SIGMA)
+                min_chunk=vts.TUNE_MIN_CHUNK, likely=vts.TUNE_LIKELY_SIGMA,
+                no_balance=vts.TUNE_NO_BALANCE)
     try:
         for k, v in kw.items():
             vts.set_tuning(keys[k], v)

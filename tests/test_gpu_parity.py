@@ -53,6 +53,27 @@ def test_transform_config5_full():
 
 
 # ---------------------------------------------------------------------------
+# length-balanced placement of rows (256 * s rows, one workgroup per row):
+# every row must be taken exactly once, with the placement on and off
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,rows,width", [(3, 512, 16384), (3, 1024, 8192), (4, 768, 16384),
+                                            (5, 512, 8192), (3, 4096, 4096)])
+@pytest.mark.parametrize("balance", [True, False])
+def test_balanced_placement(cfg, rows, width, balance):
+    wl = workloads.make(cfg, rows=rows, width=width)
+    say(f"config {cfg} rows {rows} width {width} balance {balance}")
+    with tuning(nsplit=1, no_balance=0 if balance else 1):
+        if wl.kind == "varlen":
+            idx, vals, stats = run_varlen(wl)
+            errs = check_varlen(wl, idx, vals)
+        else:
+            out, raw, stats = run_transform(wl)
+            errs = check_transform_wl(wl, out, raw)
+    _assert_ok(errs)
+
+
+# ---------------------------------------------------------------------------
 # every internal path, forced, on reduced workloads
 # ---------------------------------------------------------------------------
 

@@ -164,8 +164,10 @@ def test_tuning_switches(lib):
     assert lib.vts_set_tuning(vts.TUNE_NSPLIT, 33) == INVALID
     assert lib.vts_set_tuning(vts.TUNE_FORCE_PATH, 3) == INVALID
     assert lib.vts_set_tuning(vts.TUNE_LDS_SLOTS, 10) == INVALID
+    assert lib.vts_set_tuning(vts.TUNE_LDS_SLOTS, 3841) == INVALID
+    assert lib.vts_set_tuning(vts.TUNE_NO_BALANCE, 2) == INVALID
     for key in (vts.TUNE_NSPLIT, vts.TUNE_FORCE_PATH, vts.TUNE_LDS_SLOTS, vts.TUNE_SPILL_SLOTS,
-                vts.TUNE_SAMPLE_SIGMA):
+                vts.TUNE_SAMPLE_SIGMA, vts.TUNE_NO_BALANCE):
         assert lib.vts_set_tuning(key, 0) == OK
     # the forced split count changes the workspace size accordingly
     base = lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0)

@@ -29,6 +29,7 @@ OK, WARN_HINT_DISCARDED = 0, 1
 TUNE_NSPLIT, TUNE_FORCE_PATH, TUNE_LDS_SLOTS, TUNE_SPILL_SLOTS, TUNE_SAMPLE_SIGMA = 1, 2, 3, 4, 5
 TUNE_MIN_CHUNK = 6
 TUNE_LIKELY_SIGMA = 7
+TUNE_NO_BALANCE = 8
 
 _DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 

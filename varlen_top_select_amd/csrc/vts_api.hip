@@ -30,6 +30,7 @@ struct Tuning {
     int32_t sigma_tenths = 0;
     int32_t min_chunk = 0;
     int32_t likely_tenths = 0;
+    int32_t no_balance = 0;
 } g_tune;
 
 int32_t plan_nsplit(int64_t num_rows, int64_t width) {
@@ -101,6 +102,11 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
     p.min_chunk = g_tune.min_chunk > 0 ? g_tune.min_chunk : MIN_CHUNK;
     p.num_units = (int32_t)(num_rows * ns);
     p.units_per_xcd = (p.num_units + 7) / 8;
+    // length-balanced row placement: one workgroup per row, whole slots on all
+    // 256 CUs (2..4 rows per CU, all resident at once)
+    p.balance = (ns == 1 && num_rows % BALANCE_CUS == 0 && num_rows >= 2 * BALANCE_CUS &&
+                 num_rows <= 4 * BALANCE_CUS && g_tune.no_balance == 0)
+                    ? 1 : 0;
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
     p.hi_cap = HI_SLOTS;
     p.lo_cap = LO_SLOTS;
@@ -302,6 +308,10 @@ int vts_set_tuning(int32_t key, int64_t value) {
         case VTS_TUNE_LIKELY_SIGMA:
             if (value < 0 || value > 1000) return VTS_ERR_INVALID;
             g_tune.likely_tenths = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_NO_BALANCE:
+            if (value < 0 || value > 1) return VTS_ERR_INVALID;
+            g_tune.no_balance = (int32_t)value;
             return VTS_OK;
         case VTS_TUNE_MIN_CHUNK:
             if (value != 0 && (value < 256 || value > (1 << 20))) return VTS_ERR_INVALID;

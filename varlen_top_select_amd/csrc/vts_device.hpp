@@ -18,7 +18,7 @@ constexpr int CAP = 3840;             // on-chip candidate slots per workgroup
 constexpr int STAGE = 96;             // staged 16-byte vectors per wave
 constexpr int STAGE_DRAIN = 32;       // a wave drains once this many are staged
 constexpr int SAMPLE = 4096;          // sampled keys per row: 64 blocks of 64 columns
-constexpr int SAMPLE_BLOCK = 64;
+constexpr int SAMPLE_BLOCK = 64;      // columns per sample block
 constexpr int SAMPLE_BLOCKS = SAMPLE / SAMPLE_BLOCK;
 constexpr int SPT = SAMPLE / NT;      // sampled keys per thread (16)
 constexpr int MAX_SPLIT = 32;         // workgroups per row, at most
@@ -154,8 +154,13 @@ __device__ __forceinline__ uint32_t wave_ticket_n(uint32_t* counter, uint32_t cn
 // their space: the queues exist only between two selections, and the
 // histogram is cleared again after them.
 struct Smem {
-    uint32_t key[CAP];
-    uint32_t idx[CAP];
+    union {
+        struct {
+            uint32_t key[CAP];
+            uint32_t idx[CAP];
+        };
+        uint32_t cand_words[2 * CAP];  // both arrays, before any candidate exists
+    };
     union {
         uint32_t hist[HIST_WORDS];
         struct {
@@ -254,6 +259,17 @@ __device__ __forceinline__ void block_minmax(Smem& sm, uint32_t& lo, uint32_t& h
         lo = sm.wmin[i] < lo ? sm.wmin[i] : lo;
         hi = sm.wmax[i] > hi ? sm.wmax[i] : hi;
     }
+}
+
+// Copies of the first-pass histogram of block_select_pair, in the candidate
+// arrays (free until candidates arrive); the stride shifts each copy by one
+// LDS bank.
+constexpr int SPREAD_COPIES = 4;
+constexpr int SPREAD_STRIDE = NBINS + 1;
+static_assert(SPREAD_COPIES * SPREAD_STRIDE <= 2 * CAP, "copies fit in the candidate arrays");
+
+__device__ __forceinline__ void spread_clear(Smem& sm) {
+    for (int j = threadIdx.x; j < SPREAD_COPIES * SPREAD_STRIDE; j += NT) sm.cand_words[j] = 0;
 }
 
 // Zeroes the selection histogram; every select leaves it zeroed again.
@@ -375,7 +391,21 @@ __device__ __forceinline__ void block_select_pair(Smem& sm, Visit visit, uint32_
     static_assert(W2 >= 1 && W2 <= 9 && BITS - RBITS - W2 >= 0, "digit widths");
     constexpr int S1 = BITS - RBITS, S2 = S1 - W2;
     constexpr uint32_t M2 = (1u << W2) - 1u;
-    visit([&](uint32_t key) { atomicAdd(&sm.hist[hslot(key >> S1)], 1u); });
+    // Pass 1 counts into SPREAD_COPIES copies of the histogram (lane l into
+    // copy l % SPREAD_COPIES), which the candidate arrays hold before any
+    // candidate exists: the top 10 bits of typical keys fall into a few digits,
+    // and one copy would serialize many lanes of an atomic on one address.
+    // The copies are then summed into the histogram (spread_clear zeroed them).
+    uint32_t* spread = sm.cand_words;
+    const uint32_t copy = (lane_id() % SPREAD_COPIES) * SPREAD_STRIDE;
+    visit([&](uint32_t key) { atomicAdd(&spread[copy + (key >> S1)], 1u); });
+    lds_sync();
+    for (int b = threadIdx.x; b < NBINS; b += NT) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int c = 0; c < SPREAD_COPIES; ++c) t += spread[c * SPREAD_STRIDE + b];
+        sm.hist[hslot(b)] = t;
+    }
     lds_sync();
     if (threadIdx.x < 64) {
         uint32_t d1, a1, d2, a2;

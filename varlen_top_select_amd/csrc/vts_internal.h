@@ -16,6 +16,14 @@ constexpr int HI_SLOTS = 8192;
 constexpr int LO_SLOTS = 4096;
 constexpr int WSCAP = HI_SLOTS + LO_SLOTS;
 
+// Compute units of an MI355X: 8 XCDs of 32.  Block b of a launch goes to XCD
+// b % 8, and there the k-th block (b = 8k + x) to compute unit k % 32 while
+// the first blocks fill the device, so blocks k, k + 32, k + 64, ... of an
+// XCD share a compute unit.
+constexpr int BALANCE_XCDS = 8;
+constexpr int BALANCE_CUS_PER_XCD = 32;
+constexpr int BALANCE_CUS = BALANCE_XCDS * BALANCE_CUS_PER_XCD;
+
 struct Params {
     // score rows
     const void* x;
@@ -45,6 +53,7 @@ struct Params {
     int32_t min_chunk;  // a row gets ceil(n / min_chunk) workgroups, at most nsplit
     int32_t num_units;  // num_rows * nsplit
     int32_t units_per_xcd;
+    int32_t balance;    // 1: rows are assigned to workgroups by length (see balanced_row)
     int32_t lds_cap;    // on-chip upper-rung slots used before spilling (<= CAP)
     int32_t hi_cap;     // upper-rung slots in all (<= HI_SLOTS) before re-filtering
     int32_t lo_cap;     // lower-rung slots (<= LO_SLOTS) before re-filtering

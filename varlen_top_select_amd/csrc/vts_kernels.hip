@@ -51,12 +51,23 @@ struct VarlenPolicy {
     // FlashInfer top_k_varlen doc, `seq_lens`: row t of request i ranks its
     // first max(0, (seq_lens[i] - next_n + t + 1) // compress_ratio) columns,
     // clamped to the width.
-    __device__ __forceinline__ static void window(const Params& p, int r, int64_t& base, int64_t& n) {
-        const int i = r / p.next_n, t = r - i * p.next_n;
-        const int64_t num = (int64_t)gload(p.seq_lens + i) - p.next_n + t + 1;
-        int64_t v = num <= 0 ? 0 : num / p.cr;
+    // fetch issues the row's loads, finish computes the window from them
+    struct Raw {
+        int32_t seq;
+    };
+    __device__ __forceinline__ static Raw fetch(const Params& p, int r) {
+        return Raw{gload(p.seq_lens + r / p.next_n)};
+    }
+    __device__ __forceinline__ static void finish(const Params& p, int r, Raw f, int64_t& base,
+                                                  int64_t& n) {
+        const int t = r % p.next_n;
+        const int64_t num = (int64_t)f.seq - p.next_n + t + 1;  // <= seq when positive
+        const int64_t v = num <= 0 ? 0 : (int64_t)((uint32_t)num / (uint32_t)p.cr);
         n = v < p.width ? v : p.width;
         base = 0;
+    }
+    __device__ __forceinline__ static void window(const Params& p, int r, int64_t& base, int64_t& n) {
+        finish(p, r, fetch(p, r), base, n);
     }
     template <int DT>
     __device__ __forceinline__ static void emit(const Params& p, int r, int64_t base, uint32_t pos, int32_t col,
@@ -73,9 +84,19 @@ struct VarlenPolicy {
 struct PagePolicy {
     // Window [row_start, row_start + n), n = clamp(length, 0, width - row_start);
     // a start outside [0, width] is an empty row.
+    struct Raw {
+        int32_t start, len;
+    };
+    __device__ __forceinline__ static Raw fetch(const Params& p, int r) {
+        return Raw{p.row_starts ? gload(p.row_starts + r) : 0, gload(p.lengths + r)};
+    }
     __device__ __forceinline__ static void window(const Params& p, int r, int64_t& base, int64_t& n) {
-        const int64_t b = p.row_starts ? (int64_t)gload(p.row_starts + r) : 0;
-        const int64_t len = gload(p.lengths + r);
+        finish(p, r, fetch(p, r), base, n);
+    }
+    __device__ __forceinline__ static void finish(const Params& p, int, Raw f, int64_t& base,
+                                                  int64_t& n) {
+        const int64_t b = f.start;
+        const int64_t len = f.len;
         if (b < 0 || b > p.width) {
             base = 0;
             n = 0;
@@ -230,18 +251,25 @@ struct Sample {
 
 template <int DT>
 __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* row, int64_t n,
-                                            Sample& S) {
+                                            uint32_t salt, Sample& S) {
     // one straight run of loads for both cases (positions clamped, so all are
-    // in flight at once); short rows mask out positions >= n
+    // in flight at once); short rows mask out positions >= n.  Block b starts
+    // at (b * (n - 64) + shift) / 64, shift in [0, n - 64) from the salt: the
+    // blocks stay evenly spaced over the row, at an offset that differs from
+    // row to row (see StepOrder).
     const bool whole = n <= SAMPLE;
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const uint64_t span = whole ? 0u : (uint64_t)(n - SAMPLE_BLOCK);  // < 2^31
+    const uint64_t shift = (salt * span) >> 32;
+    static_assert(NT % SAMPLE_BLOCK == 0, "whole sample blocks per pass");
+    constexpr int BPJ = NT / SAMPLE_BLOCK;  // blocks read per pass of the workgroup
+    const int w = threadIdx.x / SAMPLE_BLOCK, lane = threadIdx.x % SAMPLE_BLOCK;
     S.vmask = 0;
 #pragma unroll
     for (int j = 0; j < SPT; ++j) {
-        const int64_t b = w + j * WAVES;
+        const uint64_t b = (uint64_t)(w + j * BPJ);
         const int64_t pw = threadIdx.x + (int64_t)j * NT;
         const int64_t pos = whole ? (pw < n ? pw : n - 1)
-                                  : b * (n - SAMPLE_BLOCK) / (SAMPLE_BLOCKS - 1) + lane;
+                                  : (int64_t)((b * span + shift) / SAMPLE_BLOCKS) + lane;
         S.key[j] = gload(row + pos);
         if (!whole || pw < n) S.vmask |= 1u << j;
     }
@@ -509,17 +537,20 @@ __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (
                                            const RungTest<DT, true>& test, uint32_t& sc) {
     static_assert(STAGE_DRAIN + 64 <= STAGE, "staging queue bound");
     const uint32_t base = (threadIdx.x >> 6) * STAGE;
+    const uint32_t l = lane_id();
 #pragma unroll
     for (int u = 0; u < Traits<DT>::U; ++u) {
         const bool hit = vec_max_raw<DT>(R[u]) >= test.a;
         const uint64_t m = ballot(hit);
-        if (m == 0) continue;  // uniform
-        if (hit) {
-            const uint32_t pos = base + sc + mbcnt(m);
-            sm.stage.vec[pos] = R[u];
-            sm.stage.v[pos] = first + (uint32_t)u * NT + threadIdx.x;
-        }
-        sc += (uint32_t)__popcll(m);
+        const uint32_t nh = (uint32_t)__popcll(m);
+        // Every lane writes, without branching: hits to slots [sc, sc + nh) in
+        // lane order, the others to [sc + nh, sc + 64), which later entries
+        // overwrite and the drain never reads.
+        const uint32_t below = mbcnt(m);
+        const uint32_t pos = base + sc + (hit ? below : nh + (l - below));
+        sm.stage.vec[pos] = R[u];
+        sm.stage.v[pos] = first + (uint32_t)u * NT + threadIdx.x;
+        sc += nh;
         if (sc >= (uint32_t)STAGE_DRAIN) {
             drain_stage<DT>(sm, B, col0, test, sc);
             sc = 0;
@@ -531,11 +562,33 @@ __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (
 // in RA (or in flight to it): two register sets in turn, the next step's loads
 // are in flight while the current one is filtered.  FAST (both rungs >= +0)
 // uses the staged vector filter, otherwise the element filter.
+// Order in which a unit visits its steps: step s is the body's step
+// (s + rot) mod nsteps.  Units start their streams at spread-out offsets
+// (rot from a hash of the unit index), so at any moment the workgroups of a
+// batch read different address ranges of their rows instead of all reading
+// the same offset of equally spaced rows, which would load a few HBM channels
+// and leave the rest idle.
+struct StepOrder {
+    uint32_t nsteps, rot;
+    __device__ __forceinline__ uint32_t first(uint32_t s, uint32_t step) const {
+        uint32_t t = s + rot;
+        if (t >= nsteps) t -= nsteps;
+        return t * step;
+    }
+};
+
+__device__ __forceinline__ uint32_t spread_hash(uint32_t x) { return x * 0x9E3779B1u; }
+
+// The streaming loop over a unit's body vectors, starting with the first step
+// of `order` already in RA (or in flight to it): two register sets in turn,
+// the next step's loads are in flight while the current one is filtered.
+// FAST (both rungs >= +0) uses the staged vector filter, otherwise the element
+// filter.
 template <int DT, bool FAST>
 __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[Traits<DT>::U],
                                             u32x4 (&RB)[Traits<DT>::U],
                                             __amdgpu_buffer_rsrc_t rs, uint32_t nvec,
-                                            uint32_t col0, const Rungs& G) {
+                                            uint32_t col0, const Rungs& G, const StepOrder& order) {
     constexpr uint32_t STEP = (uint32_t)NT * Traits<DT>::U;
     const RungTest<DT, FAST> test(G);
     uint32_t sc = 0;  // staged vectors of this wave (FAST)
@@ -547,17 +600,20 @@ __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[
             filter_step<DT, false>(sm, B, R, vs, nvec, col0, test);
         }
     };
-    // Step 0 is filtered before the loop, so on entry and on the back edge
-    // alike exactly the loads of RB are in flight at the loop header: the
-    // compiler's wait counts then let them stay in flight while RA is filtered.
-    load_step(RB, rs, STEP);
-    step(RA, 0);
-    for (uint32_t vs = STEP; vs < nvec; vs += 2 * STEP) {
-        load_step(RA, rs, vs + STEP);
-        step(RB, vs);
-        if (vs + STEP >= nvec) break;
-        load_step(RB, rs, vs + 2 * STEP);
-        step(RA, vs + STEP);
+    // On entry the loads of the first step (RA) are in flight.  The first step
+    // is filtered before the loop, so on entry and on the back edge alike
+    // exactly the loads of RB are in flight at the loop header: the compiler's
+    // wait counts then let them stay in flight while RA is filtered.  (A load
+    // for a step past the last one re-reads an earlier step: harmless.)
+    const uint32_t ns = order.nsteps;
+    load_step(RB, rs, order.first(1, STEP));
+    step(RA, order.first(0, STEP));
+    for (uint32_t s = 1; s < ns; s += 2) {
+        load_step(RA, rs, order.first(s + 1, STEP));
+        step(RB, order.first(s, STEP));
+        if (s + 1 >= ns) break;
+        load_step(RB, rs, order.first(s + 2, STEP));
+        step(RA, order.first(s + 1, STEP));
     }
     if constexpr (FAST) {
         if (sc) drain_stage<DT>(sm, B, col0, test, sc);
@@ -745,15 +801,25 @@ __device__ __forceinline__ void ingest_global(Smem& sm, int k, const uint32_t* g
 // ---------------------------------------------------------------------------
 
 // Enumerates candidate entries (key, col) with wave-uniform trip counts.
+// The candidates in LDS slots [0, n), n <= CAP, read once into registers
+// (slot j * NT + threadIdx.x in register j): the selection passes and the
+// emission then visit registers instead of re-reading LDS.
 struct LdsSrc {
+    static constexpr int J = (CAP + NT - 1) / NT;
     uint32_t n;
-    template <class F>
-    __device__ __forceinline__ void for_each(Smem& sm, F f) const {
-        for (uint32_t b = 0; b < n; b += NT) {
-            const uint32_t q = b + threadIdx.x;
-            const bool ok = q < n;
-            f(ok, ok ? sm.key[q] : 0u, ok ? sm.idx[q] : 0u);
+    uint32_t key[J], idx[J];
+    __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t n_) : n(n_) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const uint32_t q = (uint32_t)j * NT + threadIdx.x;
+            key[j] = q < n ? sm.key[q] : 0u;
+            idx[j] = q < n ? sm.idx[q] : 0u;
         }
+    }
+    template <class F>
+    __device__ __forceinline__ void for_each(Smem&, F f) const {
+#pragma unroll
+        for (int j = 0; j < J; ++j) f((uint32_t)j * NT + threadIdx.x < n, key[j], idx[j]);
     }
 };
 
@@ -775,16 +841,24 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         sm.cnt_a = 0;
         sm.cnt_b = 0;
     }
-    __syncthreads();
+    lds_sync();
+    // Each thread counts its keys > K and == K; one bit-sliced wave prefix and
+    // one LDS ticket per wave and list give every thread its first output
+    // slots, and its keys are written in order from there.
+    uint32_t ngt = 0, neq = 0;
+    src.for_each(sm, [&](bool ok, uint32_t key, uint32_t) {
+        ngt += (ok && key > K) ? 1u : 0u;
+        neq += (ok && key == K) ? 1u : 0u;
+    });
+    uint32_t og = wave_ticket_n(&sm.cnt_a, ngt);
+    uint32_t oe = wave_ticket_n(&sm.cnt_b, neq);
     src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
-        uint64_t m;
-        const bool isgt = ok && key > K;
-        const uint32_t pg = wave_ticket(&sm.cnt_a, isgt, m);
-        if (isgt) Policy::template emit<DT>(p, r, base, pg, (int32_t)col, from_key<DT>(key));
-        const bool iseq = ok && key == K;
-        const uint32_t e = wave_ticket(&sm.cnt_b, iseq, m);
-        if (iseq && e < need_eq)
-            Policy::template emit<DT>(p, r, base, gt + e, (int32_t)col, from_key<DT>(key));
+        const bool isgt = ok && key > K, iseq = ok && key == K;
+        const uint32_t pos = isgt ? og : gt + oe;
+        if (isgt || (iseq && oe < need_eq))
+            Policy::template emit<DT>(p, r, base, pos, (int32_t)col, from_key<DT>(key));
+        og += isgt ? 1u : 0u;
+        oe += iseq ? 1u : 0u;
     });
 }
 
@@ -807,7 +881,91 @@ __device__ __forceinline__ void whole_row(Smem& sm, const Params& p, int r, int6
     __syncthreads();
     const uint32_t cand = sm.cand_n;
     __syncthreads();
-    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc{cand});
+    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, cand));
+}
+
+// Length-balanced placement of rows (one workgroup per row, R = 256 * s rows,
+// 2 <= s <= 4).  Rows ordered by valid length -- longest first, in 32 length
+// buckets, by row index within a bucket -- are dealt to compute units in a
+// snake: the workgroups that share compute unit g (see BALANCE_CUS) take ranks
+// g, 511 - g, 512 + g, 1023 - g, ..., so every unit's rows add up to about the
+// same number of columns and no unit is left with only long rows.  Every
+// workgroup derives the same ranking from the row lengths, and the map from
+// blocks to ranks is a bijection, so each row is taken exactly once; the
+// placement only changes speed.  Every thread must call it.
+template <class Policy>
+__device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t bid) {
+    constexpr int NB = 32;
+    constexpr int MAXPER = 4;  // rows per thread (R <= 4 * NT)
+    const int per = p.num_rows / NT;
+    // scratch in the histogram, which is cleared before its first use
+    uint32_t* cnt = sm.hist;          // NB bucket counts
+    uint32_t* wcnt = sm.hist + 2 * NB;  // per chunk and wave: rows of the wanted bucket
+    uint32_t bk[MAXPER];
+    // every row's loads first (their latency is the cost here), then the lengths
+    typename Policy::Raw raw[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i)
+        raw[i] = Policy::fetch(p, i < per ? (int)threadIdx.x + i * NT : 0);
+    const float scale = (float)NB / (float)(p.width + 1);
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        int64_t base, n;
+        Policy::finish(p, (int)threadIdx.x + i * NT, raw[i], base, n);
+        uint32_t q = (uint32_t)((float)n * scale);  // 0..NB-1, longer rows higher
+        q = q > NB - 1 ? NB - 1 : q;
+        bk[i] = i < per ? NB - 1 - q : (uint32_t)NB;  // 0: longest; NB: no row
+    }
+    if (threadIdx.x < NB) cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) sm.total = 0xFFFFFFFFu;
+    lds_sync();
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i)
+        if (i < per) atomicAdd(&cnt[bk[i]], 1u);
+    lds_sync();
+    const uint32_t x = bid % BALANCE_XCDS, k = bid / BALANCE_XCDS;
+    const uint32_t g = x * BALANCE_CUS_PER_XCD + k % BALANCE_CUS_PER_XCD;
+    const uint32_t j = k / BALANCE_CUS_PER_XCD;
+    const uint32_t rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
+    // bucket holding the rank and the rank within it (the same in every thread)
+    uint32_t acc = 0, want = NB, m = 0;
+    for (int b = 0; b < NB; ++b) {
+        const uint32_t c = cnt[b];
+        if (want == NB && rank < acc + c) {
+            want = (uint32_t)b;
+            m = rank - acc;
+        }
+        acc += c;
+    }
+    // The m-th row of that bucket in row order; row i * NT + t is thread t's
+    // bk[i].  One ballot per chunk i, all counts published at once.
+    const uint32_t w = threadIdx.x >> 6;
+    uint64_t mask[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        mask[i] = ballot(bk[i] == want);
+        if (i < per && lane_id() == 0) wcnt[i * WAVES + w] = (uint32_t)__popcll(mask[i]);
+    }
+    lds_sync();
+    uint32_t before = 0;  // rows of the bucket before chunk i, wave w
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        if (i >= per) break;
+        uint32_t mine = 0, chunk = 0;
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) {
+            const uint32_t c = wcnt[i * WAVES + v];
+            mine += (uint32_t)v < w ? c : 0u;
+            chunk += c;
+        }
+        const uint32_t r0 = before + mine + mbcnt(mask[i]);
+        if (bk[i] == want && r0 == m) sm.total = (uint32_t)((int)threadIdx.x + i * NT);
+        before += chunk;
+    }
+    lds_sync();
+    const int row = (int)sm.total;
+    lds_sync();  // sm.total is rewritten later
+    return (row >= 0 && row < p.num_rows) ? row : (int)(bid % (uint32_t)p.num_rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -824,8 +982,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const uint32_t bid = blockIdx.x;
     const uint32_t unit = (bid & 7u) * (uint32_t)p.units_per_xcd + (bid >> 3);
     if (unit >= (uint32_t)p.num_units) return;
-    const int r = (int)(unit / (uint32_t)p.nsplit);
-    const int c = (int)(unit - (uint32_t)r * (uint32_t)p.nsplit);
+    const int r = p.balance ? balanced_row<Policy>(sm, p, bid) : (int)(unit / (uint32_t)p.nsplit);
+    const int c = p.balance ? 0 : (int)(unit - (uint32_t)r * (uint32_t)p.nsplit);
 
     int64_t base, n;
     Policy::window(p, r, base, n);
@@ -851,21 +1009,28 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     constexpr int U = Traits<DT>::U;
 
     // The sample's loads go out first, then the first streaming step's, which
-    // stays in flight while the rungs are computed.
+    // stay in flight while the rungs are computed.
     Sample S;
-    sample_load<DT>(row, n, S);
+    sample_load<DT>(row, n, spread_hash((uint32_t)r), S);
     u32x4 RA[U], RB[U];
     bool refiltered = p.force_path == FORCE_CAREFUL;
     // (always issued, also where the careful filter will ignore it: straight-line
     // code keeps the wait counts exact)
     const __amdgpu_buffer_rsrc_t rs = body_rsrc(vb, nvec * 16u);
-    load_step(RA, rs, 0u);
+    constexpr uint32_t STEP = (uint32_t)NT * U;
+    StepOrder order;
+    order.nsteps = (nvec + STEP - 1) / STEP;
+    order.rot = order.nsteps > 1
+                    ? (uint32_t)(((uint64_t)spread_hash(unit) * order.nsteps) >> 32)
+                    : 0u;
+    load_step(RA, rs, order.first(0, STEP));
     if (threadIdx.x == 0) {
         sm.cand_n = 0;
         sm.lo_n = 0;
     }
-    hist_clear(sm);  // every select leaves the histogram zeroed again
-    lds_sync();      // the loads stay in flight
+    hist_clear(sm);    // every select leaves the histogram zeroed again
+    spread_clear(sm);  // the sample select's first-pass copies
+    lds_sync();        // the loads stay in flight
     const Rungs G = sample_rungs<DT>(sm, p, n, S);
 
     uint32_t nh, nl, lcap;  // upper / lower candidates, on-chip part of the upper ones
@@ -874,9 +1039,9 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         constexpr uint32_t SIGN = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
         if (nvec == 0) {
         } else if (G.T & G.T2 & SIGN) {  // both rungs >= +0: raw-bit compares
-            stream_unit<DT, true>(sm, B, RA, RB, rs, nvec, col0, G);
+            stream_unit<DT, true>(sm, B, RA, RB, rs, nvec, col0, G, order);
         } else {
-            stream_unit<DT, false>(sm, B, RA, RB, rs, nvec, col0, G);
+            stream_unit<DT, false>(sm, B, RA, RB, rs, nvec, col0, G, order);
         }
         filter_scalars<DT>(sm, B, row, s.t0, s.t1, G);
         __syncthreads();  // also completes the workspace stores of every thread
@@ -922,7 +1087,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         __syncthreads();
         const uint32_t m = sm.cand_n;
         __syncthreads();
-        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc{m});
+        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, m));
         return;
     }
 
@@ -1002,7 +1167,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     __syncthreads();
     const uint32_t m = sm.cand_n;
     __syncthreads();
-    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc{m});
+    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, m));
 }
 
 // ---------------------------------------------------------------------------
