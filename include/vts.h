@@ -188,7 +188,7 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *   VTS_TUNE_FORCE_PATH   0 normal, 1 every chunk uses the compaction filter,
  *                         2 every row is re-selected over the whole row
  *   VTS_TUNE_LDS_SLOTS    on-chip candidate slots before spilling to the
- *                         workspace (0 = default; 64..3840)
+ *                         workspace (0 = default; 64..3776)
  *   VTS_TUNE_SPILL_SLOTS  workspace candidate slots per workgroup and rung
  *                         before a chunk is re-filtered (0 = default; 64..8192)
  *   VTS_TUNE_SAMPLE_SIGMA margin of the safe threshold rung in tenths of a

@@ -14,9 +14,9 @@ namespace vts {
 
 constexpr int NT = 256;               // threads per workgroup: 4 wave64
 constexpr int WAVES = NT / 64;
-constexpr int CAP = 3840;             // on-chip candidate slots per workgroup
-constexpr int STAGE = 96;             // staged 16-byte vectors per wave
-constexpr int STAGE_DRAIN = 32;       // a wave drains once this many are staged
+constexpr int CAP = 3776;             // on-chip candidate slots per workgroup
+constexpr int STAGE = 128;            // staged 16-byte vectors per wave
+constexpr int STAGE_DRAIN = 64;       // a wave drains one full round at this many
 constexpr int SAMPLE = 4096;          // sampled keys per row: 64 blocks of 64 columns
 constexpr int SAMPLE_BLOCK = 64;      // columns per sample block
 constexpr int SAMPLE_BLOCKS = SAMPLE / SAMPLE_BLOCK;

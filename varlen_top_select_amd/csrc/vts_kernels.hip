@@ -472,10 +472,10 @@ __device__ __forceinline__ int32_t vec_max_raw(const u32x4& q) {
     }
 }
 
-// Drains a wave's staging queue (slots [0, sc), sc <= STAGE, wave-uniform):
-// in rounds of 64, lane l takes slot l of the round and runs the element
-// filter on its vector; the candidates get LDS tickets as in filter_step.
-// Every lane of the wave calls it; no barrier (the queue is the wave's own).
+// Drains slots [0, sc) of a wave's staging queue (sc <= 64, wave-uniform) in
+// one round: lane l takes slot l and runs the element filter on its vector;
+// the candidates get LDS tickets as in filter_step.  Every lane of the wave
+// calls it; no barrier (the queue is the wave's own).
 template <int DT>
 __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col0,
                                             const RungTest<DT, true>& test, uint32_t sc) {
@@ -483,8 +483,8 @@ __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col
     constexpr uint32_t F = fail_word<DT>();
     const uint32_t base = (threadIdx.x >> 6) * STAGE;
     const uint32_t l = lane_id();
-    for (uint32_t r0 = 0; r0 < sc; r0 += 64) {
-        const uint32_t i = r0 + l;
+    {
+        const uint32_t i = l;
         u32x4 q = u32x4{F, F, F, F};
         uint32_t v = 0;
         if (i < sc) {
@@ -527,10 +527,11 @@ __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col
 
 // One streaming step with both rungs >= +0.  Per vector: the largest raw
 // element against the lower rung; the (few) vectors holding a candidate are
-// appended to the wave's staging queue in LDS (ballot + mbcnt positions), and
-// the queue is drained once it holds STAGE_DRAIN vectors, which keeps it below
-// STAGE_DRAIN + 64 <= STAGE.  The per-element work then runs on full rounds
-// of staged vectors instead of on every element of the step.
+// appended to the wave's staging queue in LDS (ballot + mbcnt positions).
+// Once 64 are queued, one full round of 64 is drained and the rest (fewer
+// than 64) moves to the front, so the queue stays below 64 + 64 <= STAGE and
+// the per-element work runs on full rounds of staged vectors instead of on
+// every element of the step.
 template <int DT>
 __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (&R)[Traits<DT>::U],
                                            uint32_t first, uint32_t col0,
@@ -552,8 +553,14 @@ __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (
         sm.stage.v[pos] = first + (uint32_t)u * NT + threadIdx.x;
         sc += nh;
         if (sc >= (uint32_t)STAGE_DRAIN) {
-            drain_stage<DT>(sm, B, col0, test, sc);
-            sc = 0;
+            drain_stage<DT>(sm, B, col0, test, STAGE_DRAIN);
+            sc -= STAGE_DRAIN;
+            if (l < sc) {  // the rest to the front (the wave's own slots, in order)
+                const u32x4 q = sm.stage.vec[base + STAGE_DRAIN + l];
+                const uint32_t v = sm.stage.v[base + STAGE_DRAIN + l];
+                sm.stage.vec[base + l] = q;
+                sm.stage.v[base + l] = v;
+            }
         }
     }
 }
@@ -804,8 +811,12 @@ __device__ __forceinline__ void ingest_global(Smem& sm, int k, const uint32_t* g
 // The candidates in LDS slots [0, n), n <= CAP, read once into registers
 // (slot j * NT + threadIdx.x in register j): the selection passes and the
 // emission then visit registers instead of re-reading LDS.
+// A second part, slots [own, n) of a workspace candidate list, can follow the
+// LDS slots [0, own): the upper list of a unit that spilled a little past the
+// on-chip slots is selected without compacting it first (n <= J * NT).
 struct LdsSrc {
-    static constexpr int J = (CAP + NT - 1) / NT;
+    static constexpr int J = 16;
+    static_assert(J * NT >= CAP, "every on-chip slot has a register");
     uint32_t n;
     uint32_t key[J], idx[J];
     __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t n_) : n(n_) {
@@ -814,6 +825,19 @@ struct LdsSrc {
             const uint32_t q = (uint32_t)j * NT + threadIdx.x;
             key[j] = q < n ? sm.key[q] : 0u;
             idx[j] = q < n ? sm.idx[q] : 0u;
+        }
+    }
+    __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t own, const uint32_t* gkey,
+                                      const uint32_t* gidx, uint32_t n_)
+        : n(n_) {
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const uint32_t q = (uint32_t)j * NT + threadIdx.x;
+            const uint32_t ql = q < own ? q : 0u, qg = q < n ? q : 0u;
+            const uint32_t kl = sm.key[ql], il = sm.idx[ql];
+            const uint32_t kg = gload(gkey + qg), ig = gload(gidx + qg);
+            key[j] = q < own ? kl : (q < n ? kg : 0u);
+            idx[j] = q < own ? il : (q < n ? ig : 0u);
         }
     }
     template <class F>
@@ -1072,6 +1096,12 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
             return;
         }
         const bool need_lo = nh < (uint32_t)p.k;
+        if (!need_lo && nh > own && nh <= (uint32_t)(LdsSrc::J * NT)) {
+            // a small spill: select over the on-chip and the spilled slots as they are
+            if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
+            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, own, gkey, gidx, nh));
+            return;
+        }
         if (nh > own || need_lo) {  // pull spilled / lower-rung candidates into LDS
             if (threadIdx.x == 0) {
                 sm.cand_n = own;
