@@ -235,51 +235,78 @@ struct Rungs {
     uint32_t T2;  // likely rung, T2 >= T
 };
 
-// Rows with at most SAMPLE columns are read whole and T = T2 is a lower bound
-// of their k-th largest key.  Longer rows read SAMPLE_BLOCKS blocks of
-// SAMPLE_BLOCK columns spread evenly over [0, n); with mu = k * SAMPLE / n, the
-// expected number of sampled keys above the row's k-th largest,
+// Short rows are read whole and T = T2 is a lower bound of their k-th largest
+// key.  Longer rows read SAMPLE_BLOCKS blocks of SAMPLE_BLOCK columns spread
+// evenly over [0, n); with mu = k * SAMPLE / n, the expected number of sampled
+// keys above the row's k-th largest,
 //   T  = the sample's q-th largest key,  q  = ceil(mu + sigma  * sqrt(mu) + 4),
 //   T2 = the sample's q2-th largest key, q2 = ceil(mu + sigma2 * sqrt(mu) + 1).
 // Keys are resolved to their top 19 bits for fp32 (a lower bound: every key
 // sharing the prefix passes, equal keys included) and exactly for 16-bit keys.
 // The loads are issued by sample_load; sample_rungs consumes them.
+//
+// The sample is read in 16-byte vectors on the row's 16-byte grid (the grid
+// starts `mis` elements before the row): a block starts at the first grid
+// point at or after its nominal column, and a whole row is the SAMPLE / VE
+// grid vectors from the one holding column 0, so "short" means n <= SAMPLE -
+// mis.  Four vector loads per thread instead of sixteen scalar ones keep the
+// address unit free for the streaming loads that follow.
+template <int DT>
 struct Sample {
-    uint32_t key[SPT];  // raw bits until sample_rungs turns them into keys
-    uint32_t vmask;     // bit j: key[j] is a sampled key
+    static constexpr int V = SPT / Traits<DT>::VE;  // vectors per thread
+    u32x4 v[V];      // raw bits until sample_rungs turns them into keys
+    uint32_t vmask;  // bit j: element j % VE of vector j / VE is a sampled key
+    bool whole;      // the whole row is sampled
 };
 
 template <int DT>
 __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* row, int64_t n,
-                                            uint32_t salt, Sample& S) {
-    // one straight run of loads for both cases (positions clamped, so all are
-    // in flight at once); short rows mask out positions >= n.  Block b starts
-    // at (b * (n - 64) + shift) / 64, shift in [0, n - 64) from the salt: the
+                                            uint32_t salt, Sample<DT>& S) {
+    // One straight run of loads for both cases, all in flight at once; a
+    // range-checked buffer over the row's grid vectors returns zeros past the
+    // last one, and vmask drops the columns outside [0, n).  Block b starts
+    // near (b * span + shift) / 64, shift in [0, span) from the salt: the
     // blocks stay evenly spaced over the row, at an offset that differs from
     // row to row (see StepOrder).
-    const bool whole = n <= SAMPLE;
-    const uint64_t span = whole ? 0u : (uint64_t)(n - SAMPLE_BLOCK);  // < 2^31
+    using raw_t = typename Traits<DT>::raw_t;
+    constexpr uint32_t VE = Traits<DT>::VE;
+    constexpr int V = Sample<DT>::V;
+    constexpr uint32_t VPB = SAMPLE_BLOCK / VE;  // vectors per block
+    static_assert(SAMPLE_BLOCK % VE == 0 && (NT * V) % VPB == 0, "whole blocks");
+    const uint32_t mis = (uint32_t)(((uintptr_t)row & 15u) / sizeof(raw_t));
+    const raw_t* grid = row - mis;  // 16-byte aligned
+    const bool whole = n <= (int64_t)(SAMPLE - mis);
+    // rows are shorter than 2^31 bytes, so the grid fits a 32-bit range
+    const uint32_t nv = (uint32_t)(((uint64_t)n + mis + VE - 1) / VE);
+    const __amdgpu_buffer_rsrc_t rs = body_rsrc(grid, nv * 16u);
+    // block starts in [0, span); a block ends by column n - 2 after rounding up
+    const uint64_t span = whole ? 0u : (uint64_t)(n - SAMPLE_BLOCK - (VE - 1));
     const uint64_t shift = (salt * span) >> 32;
-    static_assert(NT % SAMPLE_BLOCK == 0, "whole sample blocks per pass");
-    constexpr int BPJ = NT / SAMPLE_BLOCK;  // blocks read per pass of the workgroup
-    const int w = threadIdx.x / SAMPLE_BLOCK, lane = threadIdx.x % SAMPLE_BLOCK;
+    S.whole = whole;
     S.vmask = 0;
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-        const uint64_t b = (uint64_t)(w + j * BPJ);
-        const int64_t pw = threadIdx.x + (int64_t)j * NT;
-        const int64_t pos = whole ? (pw < n ? pw : n - 1)
-                                  : (int64_t)((b * span + shift) / SAMPLE_BLOCKS) + lane;
-        S.key[j] = gload(row + pos);
-        if (!whole || pw < n) S.vmask |= 1u << j;
+    for (int j = 0; j < V; ++j) {
+        const uint32_t g = threadIdx.x + (uint32_t)j * NT;  // 0 .. SAMPLE / VE - 1
+        const uint64_t b = g / VPB;
+        const uint32_t c = (uint32_t)((b * span + shift) / SAMPLE_BLOCKS);
+        const uint32_t gv = whole ? g : (c + mis + VE - 1) / VE + g % VPB;
+        S.v[j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(gv * 16u), 0, 0));
+#pragma unroll
+        for (uint32_t e = 0; e < VE; ++e) {
+            const int64_t col = (int64_t)(gv * VE + e) - (int64_t)mis;
+            if (!whole || (col >= 0 && col < n)) S.vmask |= 1u << (j * VE + e);
+        }
     }
 }
 
 template <int DT>
-__device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t n, Sample& S) {
+__device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t n,
+                                              Sample<DT>& S) {
     constexpr int BITS = Traits<DT>::BITS;
+    constexpr int VE = Traits<DT>::VE;
     uint32_t q = (uint32_t)p.k, q2 = q;
-    if (n > SAMPLE) {
+    if (!S.whole) {
         const float mu = (float)p.k * (float)SAMPLE / (float)n;
         const float sq = sqrtf(mu);
         const float qf = ceilf(mu + p.sigma * sq + 4.0f);
@@ -287,12 +314,14 @@ __device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t
         q = qf >= (float)SAMPLE ? (uint32_t)SAMPLE : (uint32_t)qf;
         q2 = q2f >= (float)q ? q : (uint32_t)q2f;
     }
+    uint32_t key[SPT];
 #pragma unroll
-    for (int j = 0; j < SPT; ++j) S.key[j] = to_key<DT>((typename Traits<DT>::raw_t)S.key[j]);
+    for (int j = 0; j < SPT; ++j)
+        key[j] = to_key<DT>((typename Traits<DT>::raw_t)vec_elem<DT>(S.v[j / VE], j % VE));
     auto visit = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < SPT; ++j)
-            if ((S.vmask >> j) & 1u) f(S.key[j]);
+            if ((S.vmask >> j) & 1u) f(key[j]);
     };
     Rungs R;
     block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(sm, visit, q, q2, R.T, R.T2);
@@ -1034,7 +1063,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
 
     // The sample's loads go out first, then the first streaming step's, which
     // stay in flight while the rungs are computed.
-    Sample S;
+    Sample<DT> S;
     sample_load<DT>(row, n, spread_hash((uint32_t)r), S);
     u32x4 RA[U], RB[U];
     bool refiltered = p.force_path == FORCE_CAREFUL;
