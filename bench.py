@@ -314,8 +314,7 @@ def main() -> int:
                      "valid_bytes_frac_of_peak": round(valid / (kern_us.mean() * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
                      "kernel_source_hash": src_hash},
         "events": {"refiltered_workgroups": stats[0], "whole_row_reselections": stats[1],
-                   "workspace_compactions": stats[2],
-                   "lower_rung_readbacks": stats[3]},
+                   "spilled_rows": stats[2], "full_list_selections": stats[3]},
     }
     if args.calibrate_copy:
         nb = args.calibrate_copy << 20

@@ -171,15 +171,17 @@ int topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_row
 /* Human-readable text of a vts_status. */
 const char* vts_status_string(int status);
 
-/* Event counters kept in a workspace, copied to `out` (host, >= 4 entries)
+/* Event counters kept in a workspace, copied to `out` (host, `count` <= 4
+ * entries)
  * with a synchronous copy on `stream`, then cleared:
  *   out[0]  workgroups whose candidates overflowed and were re-filtered
  *   out[1]  rows whose sampled threshold kept fewer than top_k candidates
  *           and that were re-selected over the whole row
- *   out[2]  rows whose candidates outgrew on-chip memory and were compacted
- *           back from the workspace
- *   out[3]  rows whose upper-rung candidates were fewer than top_k, so that
- *           the lower rung was read back */
+ *   out[2]  rows whose candidates outgrew on-chip memory (selected over the
+ *           spilled workspace slots too)
+ *   out[3]  rows with fewer than top_k keys at or above the likely threshold,
+ *           so that the whole candidate list (keys at or above the safe
+ *           threshold) was ranked */
 int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* stream);
 
 /* Tuning and test switches (process-wide; not thread-safe).  None of them
@@ -189,10 +191,11 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *                         2 every row is re-selected over the whole row
  *   VTS_TUNE_LDS_SLOTS    on-chip candidate slots before spilling to the
  *                         workspace (0 = default; 64..3776)
- *   VTS_TUNE_SPILL_SLOTS  workspace candidate slots per workgroup and rung
- *                         before a chunk is re-filtered (0 = default; 64..8192)
+ *   VTS_TUNE_SPILL_SLOTS  candidate slots per workgroup, on chip and in the
+ *                         workspace, before a chunk is re-filtered
+ *                         (0 = default; 64..8192)
  *   VTS_TUNE_SAMPLE_SIGMA margin of the safe threshold rung in tenths of a
- *                         standard deviation of the sample count (0 = 55)
+ *                         standard deviation of the sample count (0 = 50)
  *   VTS_TUNE_LIKELY_SIGMA margin of the likely rung, same unit (0 = 20; a
  *                         value >= the safe margin merges the two rungs)
  *   VTS_TUNE_MIN_CHUNK    valid columns per workgroup below which a row is not

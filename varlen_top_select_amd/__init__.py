@@ -223,8 +223,8 @@ def set_tuning(key: int, value: int) -> None:
 
 
 def workspace_stats(workspace: torch.Tensor, stream=None) -> list[int]:
-    """[re-filtered workgroups, whole-row re-selections, workspace compactions,
-    lower-rung read-backs]; clears them."""
+    """[re-filtered workgroups, whole-row re-selections, rows with spilled
+    candidates, rows ranked over the whole candidate list]; clears them."""
     out = (ctypes.c_uint32 * 4)()
     _check("vts_workspace_stats", library().vts_workspace_stats(
         workspace.data_ptr(), out, 4, _stream_ptr(stream, workspace.device)))

@@ -1,5 +1,6 @@
 """Builds the HIP library libvts.so (gfx950) in-tree with hipcc."""
 import os
+import re
 import subprocess
 import sys
 
@@ -19,13 +20,40 @@ FLAGS = [
 ]
 
 
+# The top-k kernels are sized for four workgroups of four waves per compute
+# unit (every row of a 1024-row batch resident at once) and must not spill:
+# the compiler's resource remarks are checked on every build.
+MIN_WAVES_PER_SIMD = 4
+
+
+def _check_resources(remarks: str, out: str) -> None:
+    name = None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        if name is None or "topk_kernel" not in name:
+            continue
+        m = re.search(r"Occupancy \[waves/SIMD\]: (\d+)", line)
+        if m and int(m.group(1)) < MIN_WAVES_PER_SIMD:
+            raise RuntimeError(f"{out}: {name} fits only {m.group(1)} waves per SIMD")
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and int(m.group(1)) > 0:
+            raise RuntimeError(f"{out}: {name} spills {m.group(1)} bytes per lane to scratch")
+
+
 def _compile(sources, out, verbose):
     srcs = [os.path.join(CSRC, s) for s in sources]
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
+    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
+    res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stderr)
+        raise subprocess.CalledProcessError(res.returncode, cmd)
+    _check_resources(res.stderr, out)
     os.replace(tmp, out)
 
 

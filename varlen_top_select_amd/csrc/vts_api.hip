@@ -109,20 +109,16 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
                     ? 1 : 0;
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
     p.hi_cap = HI_SLOTS;
-    p.lo_cap = LO_SLOTS;
-    if (g_tune.spill_slots > 0) {
-        p.hi_cap = g_tune.spill_slots;
-        p.lo_cap = g_tune.spill_slots < LO_SLOTS ? g_tune.spill_slots : LO_SLOTS;
-    }
+    if (g_tune.spill_slots > 0) p.hi_cap = g_tune.spill_slots;
     if (p.hi_cap < p.lds_cap) p.hi_cap = p.lds_cap;
     p.force_path = g_tune.force_path;
-    p.sigma = (g_tune.sigma_tenths > 0 ? g_tune.sigma_tenths : 55) / 10.0f;
+    p.sigma = (g_tune.sigma_tenths > 0 ? g_tune.sigma_tenths : 50) / 10.0f;
     p.sigma2 = (g_tune.likely_tenths > 0 ? g_tune.likely_tenths : 20) / 10.0f;
     if (p.sigma2 > p.sigma) p.sigma2 = p.sigma;
     p.ws_stats = reinterpret_cast<uint32_t*>(w + L.stats);
     p.ws_ticket = reinterpret_cast<uint32_t*>(w + L.ticket);
     p.ws_count = reinterpret_cast<uint32_t*>(w + L.count);
-    p.ws_count_lo = reinterpret_cast<uint32_t*>(w + L.count_lo);
+    p.ws_count_up = reinterpret_cast<uint32_t*>(w + L.count_up);
     p.ws_key = reinterpret_cast<uint32_t*>(w + L.key);
     p.ws_idx = reinterpret_cast<uint32_t*>(w + L.idx);
 }
@@ -278,7 +274,7 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
     if (hipMemcpyAsync(out, workspace, (size_t)count * 4, hipMemcpyDeviceToHost, s) != hipSuccess)
         return VTS_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return VTS_ERR_HIP;
-    if (hipMemsetAsync(workspace, 0, 16, s) != hipSuccess) return VTS_ERR_HIP;
+    if (hipMemsetAsync(workspace, 0, 4 * 4, s) != hipSuccess) return VTS_ERR_HIP;
     if (hipStreamSynchronize(s) != hipSuccess) return VTS_ERR_HIP;
     return VTS_OK;
 }

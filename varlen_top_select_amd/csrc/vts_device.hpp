@@ -17,10 +17,11 @@ constexpr int WAVES = NT / 64;
 constexpr int CAP = 3776;             // on-chip candidate slots per workgroup
 constexpr int STAGE = 128;            // staged 16-byte vectors per wave
 constexpr int STAGE_DRAIN = 64;       // a wave drains one full round at this many
-constexpr int SAMPLE = 4096;          // sampled keys per row: 64 blocks of 64 columns
+constexpr int SAMPLE = 8192;          // sampled keys per row: 128 blocks of 64 columns
 constexpr int SAMPLE_BLOCK = 64;      // columns per sample block
 constexpr int SAMPLE_BLOCKS = SAMPLE / SAMPLE_BLOCK;
-constexpr int SPT = SAMPLE / NT;      // sampled keys per thread (16)
+constexpr int SPT = SAMPLE / NT;      // sampled keys per thread (32)
+static_assert(SPT <= 32, "one mask bit per sampled key of a thread");
 constexpr int MAX_SPLIT = 32;         // workgroups per row, at most
 
 enum Dtype : int { F32 = 0, BF16 = 1, F16 = 2 };
@@ -173,13 +174,14 @@ struct Smem {
     uint32_t wmax[WAVES];
     uint32_t seg_hi[MAX_SPLIT];
     uint32_t seg_lo[MAX_SPLIT];
-    uint32_t cand_n;  // upper-rung (or compaction-filter) candidates
-    uint32_t lo_n;    // lower-rung candidates
+    uint32_t cand_n;  // candidates: keys >= the safe rung (or compaction-filter entries)
+    uint32_t up_n;    // of which keys >= the likely rung
     uint32_t cnt_a, cnt_b;
     uint32_t sel_digit, sel_above;
     uint32_t sel_digit2, sel_above2;
     uint32_t flag;
     uint32_t total;
+    uint32_t win_base, win_n;  // the placed row's window (balanced placement)
 };
 
 // Inclusive scan across the 64 lanes of a wave with DPP: Hillis-Steele inside

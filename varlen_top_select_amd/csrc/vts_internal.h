@@ -8,13 +8,11 @@
 
 namespace vts {
 
-// Candidate slots per workgroup in the workspace.  Region layout: slots
-// [0, HI_SLOTS) mirror the upper-rung candidate buffer (the first on-chip slots
-// are copied there only when a split row publishes them), slots
-// [HI_SLOTS, HI_SLOTS + LO_SLOTS) hold the lower-rung candidates.
+// Candidate slots per workgroup in the workspace: slots [0, HI_SLOTS) mirror
+// the unit's candidate list (the first, on-chip slots are copied there only
+// when a split row publishes them; later slots are where the list spills).
 constexpr int HI_SLOTS = 8192;
-constexpr int LO_SLOTS = 4096;
-constexpr int WSCAP = HI_SLOTS + LO_SLOTS;
+constexpr int WSCAP = HI_SLOTS;
 
 // Compute units of an MI355X: 8 XCDs of 32.  Block b of a launch goes to XCD
 // b % 8, and there the k-th block (b = 8k + x) to compute unit k % 32 while
@@ -54,17 +52,16 @@ struct Params {
     int32_t num_units;  // num_rows * nsplit
     int32_t units_per_xcd;
     int32_t balance;    // 1: rows are assigned to workgroups by length (see balanced_row)
-    int32_t lds_cap;    // on-chip upper-rung slots used before spilling (<= CAP)
-    int32_t hi_cap;     // upper-rung slots in all (<= HI_SLOTS) before re-filtering
-    int32_t lo_cap;     // lower-rung slots (<= LO_SLOTS) before re-filtering
+    int32_t lds_cap;    // on-chip candidate slots used before spilling (<= CAP)
+    int32_t hi_cap;     // candidate slots in all (<= HI_SLOTS) before re-filtering
     int32_t force_path;
     float sigma;        // margin of the safe rung, in standard deviations
     float sigma2;       // margin of the likely rung (<= sigma)
     // workspace
     uint32_t* ws_stats;
     uint32_t* ws_ticket;
-    uint32_t* ws_count;     // upper-rung candidates per unit
-    uint32_t* ws_count_lo;  // lower-rung candidates per unit
+    uint32_t* ws_count;     // candidates (keys >= the safe rung) per unit
+    uint32_t* ws_count_up;  // of which keys >= the likely rung, per unit
     uint32_t* ws_key;
     uint32_t* ws_idx;
 };
@@ -73,7 +70,7 @@ enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };
 
 // Workspace layout (bytes from the base): stats, tickets, counts, keys, indices.
 struct WsLayout {
-    size_t stats, ticket, count, count_lo, key, idx, total;
+    size_t stats, ticket, count, count_up, key, idx, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -84,8 +81,8 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
     L.stats = 0;
     L.ticket = 256;
     L.count = L.ticket + align256((size_t)num_rows * 4);
-    L.count_lo = L.count + align256(units * 4);
-    L.key = L.count_lo + align256(units * 4);
+    L.count_up = L.count + align256(units * 4);
+    L.key = L.count_up + align256(units * 4);
     L.idx = L.key + align256(units * WSCAP * 4);
     L.total = L.idx + align256(units * WSCAP * 4);
     return L;

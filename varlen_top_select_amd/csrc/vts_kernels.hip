@@ -196,16 +196,20 @@ __device__ __forceinline__ uint32_t vec_elem(const u32x4& q, int e) {
 }
 
 // ---------------------------------------------------------------------------
-// candidate buffers of one unit
-//   upper rung (keys >= T2): slots [0, lds_cap) in LDS, [lds_cap, hi_cap) in
-//                            the unit's workspace region;
-//   lower rung (T <= key < T2): slots [0, lo_cap) at region + HI_SLOTS.
+// the candidate list of one unit: every key >= T (the safe rung), in arrival
+// order; slots [0, lds_cap) in LDS, [lds_cap, hi_cap) in the unit's workspace
+// region.  The keys >= T2 (the likely rung) are only counted while streaming:
+// the selection ranks the list's keys >= T2 when at least k of them exist and
+// all of it otherwise, so no second list is kept.  Keeping the streaming loop
+// free of global stores matters: on this target loads and stores share one
+// wait counter, and a pending store turns the next wait for a load into a wait
+// for every access in flight, which empties the prefetch queue.
 // ---------------------------------------------------------------------------
 
 struct Buf {
     uint32_t* gkey;
     uint32_t* gidx;
-    uint32_t lds_cap, hi_cap, lo_cap;
+    uint32_t lds_cap, hi_cap;
 };
 
 __device__ __forceinline__ void put_hi(Smem& sm, const Buf& B, uint32_t pos, uint32_t key,
@@ -216,13 +220,6 @@ __device__ __forceinline__ void put_hi(Smem& sm, const Buf& B, uint32_t pos, uin
     } else if (pos < B.hi_cap) {
         gstore_at(B.gkey, pos, key);
         gstore_at(B.gidx, pos, col);
-    }
-}
-
-__device__ __forceinline__ void put_lo(const Buf& B, uint32_t pos, uint32_t key, uint32_t col) {
-    if (pos < B.lo_cap) {
-        gstore_at(B.gkey, HI_SLOTS + pos, key);
-        gstore_at(B.gidx, HI_SLOTS + pos, col);
     }
 }
 
@@ -391,19 +388,20 @@ __device__ __forceinline__ uint32_t nonneg_key(const u32x4& q, int e) {
 
 // Filters one streaming step in two passes over the thread's U vectors.
 // Pass 1 counts: each compare yields a 64-lane mask (ballot), so the wave's
-// upper- and lower-rung totals are scalar popcounts; one LDS ticket per rung
-// then reserves the wave's slots.  Pass 2 repeats the compares and, only for
-// elements whose mask is non-empty, writes each candidate at the ticket base
-// plus its rank among the wave's lanes (mbcnt).  With FAST every vector of
-// the step is valid (a partial step has been padded with fail_word).
+// totals are scalar popcounts; one LDS ticket then reserves the wave's slots
+// and the keys >= T2 are added to `upc` (the wave's count).  Pass 2 repeats
+// the compares and, only for elements whose mask is non-empty, writes each
+// candidate at the ticket base plus its rank among the wave's lanes (mbcnt).
+// With FAST every vector of the step is valid (a partial step has been padded
+// with fail_word).
 template <int DT, bool FAST>
 __device__ __forceinline__ void filter_step(Smem& sm, const Buf& B,
                                             u32x4 (&R)[Traits<DT>::U], uint32_t first,
                                             uint32_t nvec, uint32_t col0,
-                                            const RungTest<DT, FAST>& test) {
+                                            const RungTest<DT, FAST>& test, uint32_t& upc) {
     constexpr int VE = Traits<DT>::VE;
     constexpr int U = Traits<DT>::U;
-    uint32_t th = 0, ti = 0;
+    uint32_t ti = 0;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const bool ok = FAST || first + (uint32_t)u * NT + threadIdx.x < nvec;
@@ -417,19 +415,14 @@ __device__ __forceinline__ void filter_step(Smem& sm, const Buf& B,
                 mi &= okm;
                 mh &= okm;
             }
-            ti += (uint32_t)__popcll(mi);  // T2 >= T: the upper keys are among them
-            th += (uint32_t)__popcll(mh);
+            ti += (uint32_t)__popcll(mi);
+            upc += (uint32_t)__popcll(mh);  // T2 >= T: the upper keys are among them
         }
     }
     if (ti == 0) return;  // uniform
-    const uint32_t tl = ti - th;
-    uint32_t bh = 0, bl = 0;
-    if (lane_id() == 0) {
-        if (th) bh = atomicAdd(&sm.cand_n, th);
-        if (tl) bl = atomicAdd(&sm.lo_n, tl);
-    }
+    uint32_t bh = 0;
+    if (lane_id() == 0) bh = atomicAdd(&sm.cand_n, ti);
     bh = first_lane_value(bh);
-    bl = first_lane_value(bl);
     // the compares are redone below rather than kept: holding every mask of
     // the first pass would take more scalar registers than there are
 #pragma unroll
@@ -443,30 +436,22 @@ __device__ __forceinline__ void filter_step(Smem& sm, const Buf& B,
         for (int e = 0; e < VE; ++e) {
             bool in, up;
             test(R[u], e, in, up);
-            const bool h = ok && up, l = ok && in && !up;
-            uint64_t mi = ballot(in);
-            if constexpr (!FAST) mi &= ballot(ok);
+            const bool h = ok && in;
+            const uint64_t mi = ballot(h);
             if (mi == 0) continue;  // uniform
-            const uint64_t mh = ballot(h), ml = mi & ~mh;
             const uint32_t key = FAST ? nonneg_key<DT>(R[u], e) : to_key<DT>(vec_elem<DT>(R[u], e));
             const uint32_t col = colu + (uint32_t)e;
-            if (mh) {
-                const uint32_t nh = (uint32_t)__popcll(mh);
-                if (bh + nh <= B.lds_cap) {  // uniform: the usual case
-                    if (h) {
-                        const uint32_t pos = bh + mbcnt(mh);
-                        sm.key[pos] = key;
-                        sm.idx[pos] = col;
-                    }
-                } else if (h) {
-                    put_hi(sm, B, bh + mbcnt(mh), key, col);
+            const uint32_t nh = (uint32_t)__popcll(mi);
+            if (bh + nh <= B.lds_cap) {  // uniform: the usual case
+                if (h) {
+                    const uint32_t pos = bh + mbcnt(mi);
+                    sm.key[pos] = key;
+                    sm.idx[pos] = col;
                 }
-                bh += nh;
+            } else if (h) {
+                put_hi(sm, B, bh + mbcnt(mi), key, col);
             }
-            if (ml) {
-                if (l) put_lo(B, bl + mbcnt(ml), key, col);
-                bl += (uint32_t)__popcll(ml);
-            }
+            bh += nh;
         }
     }
 }
@@ -503,69 +488,60 @@ __device__ __forceinline__ int32_t vec_max_raw(const u32x4& q) {
 
 // Drains slots [0, sc) of a wave's staging queue (sc <= 64, wave-uniform) in
 // one round: lane l takes slot l and runs the element filter on its vector;
-// the candidates get LDS tickets as in filter_step.  Every lane of the wave
-// calls it; no barrier (the queue is the wave's own).
+// the candidates get one LDS ticket as in filter_step and the keys >= T2 are
+// added to `upc`.  Every lane of the wave calls it; no barrier (the queue is
+// the wave's own).
 template <int DT>
 __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col0,
-                                            const RungTest<DT, true>& test, uint32_t sc) {
+                                            const RungTest<DT, true>& test, uint32_t sc,
+                                            uint32_t& upc) {
     constexpr int VE = Traits<DT>::VE;
     constexpr uint32_t F = fail_word<DT>();
     const uint32_t base = (threadIdx.x >> 6) * STAGE;
     const uint32_t l = lane_id();
-    {
-        const uint32_t i = l;
-        u32x4 q = u32x4{F, F, F, F};
-        uint32_t v = 0;
-        if (i < sc) {
-            q = sm.stage.vec[base + i];
-            v = sm.stage.v[base + i];
-        }
-        uint32_t th = 0, ti = 0;
+    u32x4 q = u32x4{F, F, F, F};
+    uint32_t v = 0;
+    if (l < sc) {
+        q = sm.stage.vec[base + l];
+        v = sm.stage.v[base + l];
+    }
+    uint32_t ti = 0;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            bool in, up;
-            test(q, e, in, up);
-            ti += (uint32_t)__popcll(ballot(in));
-            th += (uint32_t)__popcll(ballot(up));
-        }
-        const uint32_t tl = ti - th;  // ti > 0: a staged vector holds a candidate
-        uint32_t bh = 0, bl = 0;
-        if (l == 0) {
-            if (th) bh = atomicAdd(&sm.cand_n, th);
-            if (tl) bl = atomicAdd(&sm.lo_n, tl);
-        }
-        bh = first_lane_value(bh);
-        bl = first_lane_value(bl);
-        const uint32_t colv = col0 + v * VE;
+    for (int e = 0; e < VE; ++e) {
+        bool in, up;
+        test(q, e, in, up);
+        ti += (uint32_t)__popcll(ballot(in));  // > 0: a staged vector holds a candidate
+        upc += (uint32_t)__popcll(ballot(up));
+    }
+    uint32_t bh = 0;
+    if (l == 0) bh = atomicAdd(&sm.cand_n, ti);
+    bh = first_lane_value(bh);
+    const uint32_t colv = col0 + v * VE;
 #pragma unroll
-        for (int e = 0; e < VE; ++e) {
-            bool in, up;
-            test(q, e, in, up);
-            const uint64_t mi = ballot(in);
-            if (mi == 0) continue;  // uniform
-            const uint64_t mh = ballot(up), ml = mi & ~mh;
-            const uint32_t key = nonneg_key<DT>(q, e);
-            const uint32_t col = colv + (uint32_t)e;
-            if (up) put_hi(sm, B, bh + mbcnt(mh), key, col);
-            if (in && !up) put_lo(B, bl + mbcnt(ml), key, col);
-            bh += (uint32_t)__popcll(mh);
-            bl += (uint32_t)__popcll(ml);
-        }
+    for (int e = 0; e < VE; ++e) {
+        bool in, up;
+        test(q, e, in, up);
+        const uint64_t mi = ballot(in);
+        if (mi == 0) continue;  // uniform
+        if (in) put_hi(sm, B, bh + mbcnt(mi), nonneg_key<DT>(q, e), colv + (uint32_t)e);
+        bh += (uint32_t)__popcll(mi);
     }
 }
 
 // One streaming step with both rungs >= +0.  Per vector: the largest raw
 // element against the lower rung; the (few) vectors holding a candidate are
 // appended to the wave's staging queue in LDS (ballot + mbcnt positions).
-// Once 64 are queued, one full round of 64 is drained and the rest (fewer
-// than 64) moves to the front, so the queue stays below 64 + 64 <= STAGE and
-// the per-element work runs on full rounds of staged vectors instead of on
-// every element of the step.
+// Whenever STAGE_DRAIN are queued, a round of STAGE_DRAIN is drained and the
+// rest moves to the front, so the per-element work runs on rounds of staged
+// vectors instead of on every element of the step.
 template <int DT>
 __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (&R)[Traits<DT>::U],
                                            uint32_t first, uint32_t col0,
-                                           const RungTest<DT, true>& test, uint32_t& sc) {
-    static_assert(STAGE_DRAIN + 64 <= STAGE, "staging queue bound");
+                                           const RungTest<DT, true>& test, uint32_t& sc,
+                                           uint32_t& upc) {
+    // Drains run while at least STAGE_DRAIN vectors are queued, so a vector's
+    // 64 writes start at sc <= STAGE_DRAIN - 1 and end inside the queue.
+    static_assert(STAGE_DRAIN - 1 + 64 <= STAGE && STAGE_DRAIN <= 64, "staging queue bound");
     const uint32_t base = (threadIdx.x >> 6) * STAGE;
     const uint32_t l = lane_id();
 #pragma unroll
@@ -581,8 +557,8 @@ __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (
         sm.stage.vec[pos] = R[u];
         sm.stage.v[pos] = first + (uint32_t)u * NT + threadIdx.x;
         sc += nh;
-        if (sc >= (uint32_t)STAGE_DRAIN) {
-            drain_stage<DT>(sm, B, col0, test, STAGE_DRAIN);
+        while (sc >= (uint32_t)STAGE_DRAIN) {
+            drain_stage<DT>(sm, B, col0, test, STAGE_DRAIN, upc);
             sc -= STAGE_DRAIN;
             if (l < sc) {  // the rest to the front (the wave's own slots, in order)
                 const u32x4 q = sm.stage.vec[base + STAGE_DRAIN + l];
@@ -627,13 +603,14 @@ __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[
                                             uint32_t col0, const Rungs& G, const StepOrder& order) {
     constexpr uint32_t STEP = (uint32_t)NT * Traits<DT>::U;
     const RungTest<DT, FAST> test(G);
-    uint32_t sc = 0;  // staged vectors of this wave (FAST)
+    uint32_t sc = 0;   // staged vectors of this wave (FAST)
+    uint32_t upc = 0;  // keys >= T2 seen by this wave
     auto step = [&](u32x4 (&R)[Traits<DT>::U], uint32_t vs) {
         if constexpr (FAST) {
             if (vs + STEP > nvec) pad_step<DT>(R, vs, nvec);
-            stage_step<DT>(sm, B, R, vs, col0, test, sc);
+            stage_step<DT>(sm, B, R, vs, col0, test, sc, upc);
         } else {
-            filter_step<DT, false>(sm, B, R, vs, nvec, col0, test);
+            filter_step<DT, false>(sm, B, R, vs, nvec, col0, test, upc);
         }
     };
     // On entry the loads of the first step (RA) are in flight.  The first step
@@ -652,8 +629,9 @@ __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[
         step(RA, order.first(s + 1, STEP));
     }
     if constexpr (FAST) {
-        if (sc) drain_stage<DT>(sm, B, col0, test, sc);
+        if (sc) drain_stage<DT>(sm, B, col0, test, sc, upc);
     }
+    if (lane_id() == 0 && upc) atomicAdd(&sm.up_n, upc);
 }
 
 // scalar columns [a, b) of the window (at most a few), every thread calls
@@ -665,12 +643,11 @@ __device__ __forceinline__ void filter_scalars(Smem& sm, const Buf& B,
         const int64_t c = base + threadIdx.x;
         const bool ok = c < b;
         const uint32_t key = ok ? to_key<DT>(gload(row + c)) : 0u;
-        const bool hi = ok && key >= G.T2;
-        const bool lo = ok && !hi && key >= G.T;
-        const uint32_t ph = wave_ticket_n(&sm.cand_n, hi ? 1u : 0u);
-        const uint32_t pl = wave_ticket_n(&sm.lo_n, lo ? 1u : 0u);
-        if (hi) put_hi(sm, B, ph, key, (uint32_t)c);
-        if (lo) put_lo(B, pl, key, (uint32_t)c);
+        const bool in = ok && key >= G.T;
+        const uint64_t mu = ballot(ok && key >= G.T2);
+        if (lane_id() == 0 && mu) atomicAdd(&sm.up_n, (uint32_t)__popcll(mu));
+        const uint32_t pos = wave_ticket_n(&sm.cand_n, in ? 1u : 0u);
+        if (in) put_hi(sm, B, pos, key, (uint32_t)c);
     }
 }
 
@@ -837,18 +814,18 @@ __device__ __forceinline__ void ingest_global(Smem& sm, int k, const uint32_t* g
 // ---------------------------------------------------------------------------
 
 // Enumerates candidate entries (key, col) with wave-uniform trip counts.
-// The candidates in LDS slots [0, n), n <= CAP, read once into registers
-// (slot j * NT + threadIdx.x in register j): the selection passes and the
-// emission then visit registers instead of re-reading LDS.
-// A second part, slots [own, n) of a workspace candidate list, can follow the
-// LDS slots [0, own): the upper list of a unit that spilled a little past the
-// on-chip slots is selected without compacting it first (n <= J * NT).
+// The first `own` entries come from LDS slots [0, own), the rest, up to n,
+// from slots [own, n) of a workspace list (a unit's spilled candidates); all
+// are read once into registers (entry j * NT + threadIdx.x in register j), so
+// the selection passes and the emission visit registers.  Only keys >= thr
+// are visited.  n <= J * NT.
 struct LdsSrc {
-    static constexpr int J = 16;
+    static constexpr int J = 20;
     static_assert(J * NT >= CAP, "every on-chip slot has a register");
-    uint32_t n;
+    uint32_t n, thr;
     uint32_t key[J], idx[J];
-    __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t n_) : n(n_) {
+    __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t n_, uint32_t thr_ = 0u)
+        : n(n_), thr(thr_) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const uint32_t q = (uint32_t)j * NT + threadIdx.x;
@@ -857,8 +834,8 @@ struct LdsSrc {
         }
     }
     __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t own, const uint32_t* gkey,
-                                      const uint32_t* gidx, uint32_t n_)
-        : n(n_) {
+                                      const uint32_t* gidx, uint32_t n_, uint32_t thr_)
+        : n(n_), thr(thr_) {
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const uint32_t q = (uint32_t)j * NT + threadIdx.x;
@@ -872,7 +849,8 @@ struct LdsSrc {
     template <class F>
     __device__ __forceinline__ void for_each(Smem&, F f) const {
 #pragma unroll
-        for (int j = 0; j < J; ++j) f((uint32_t)j * NT + threadIdx.x < n, key[j], idx[j]);
+        for (int j = 0; j < J; ++j)
+            f((uint32_t)j * NT + threadIdx.x < n && key[j] >= thr, key[j], idx[j]);
     }
 };
 
@@ -945,9 +923,11 @@ __device__ __forceinline__ void whole_row(Smem& sm, const Params& p, int r, int6
 // same number of columns and no unit is left with only long rows.  Every
 // workgroup derives the same ranking from the row lengths, and the map from
 // blocks to ranks is a bijection, so each row is taken exactly once; the
-// placement only changes speed.  Every thread must call it.
+// placement only changes speed.  The row's window comes back in base / n.
+// Every thread must call it.
 template <class Policy>
-__device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t bid) {
+__device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t bid,
+                                            int64_t& base, int64_t& n) {
     constexpr int NB = 32;
     constexpr int MAXPER = 4;  // rows per thread (R <= 4 * NT)
     const int per = p.num_rows / NT;
@@ -955,6 +935,7 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     uint32_t* cnt = sm.hist;          // NB bucket counts
     uint32_t* wcnt = sm.hist + 2 * NB;  // per chunk and wave: rows of the wanted bucket
     uint32_t bk[MAXPER];
+    uint32_t wb[MAXPER], wn[MAXPER];  // windows of this thread's rows (< 2^31)
     // every row's loads first (their latency is the cost here), then the lengths
     typename Policy::Raw raw[MAXPER];
 #pragma unroll
@@ -963,8 +944,10 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     const float scale = (float)NB / (float)(p.width + 1);
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
-        int64_t base, n;
-        Policy::finish(p, (int)threadIdx.x + i * NT, raw[i], base, n);
+        int64_t b, n;
+        Policy::finish(p, (int)threadIdx.x + i * NT, raw[i], b, n);
+        wb[i] = (uint32_t)b;
+        wn[i] = (uint32_t)n;
         uint32_t q = (uint32_t)((float)n * scale);  // 0..NB-1, longer rows higher
         q = q > NB - 1 ? NB - 1 : q;
         bk[i] = i < per ? NB - 1 - q : (uint32_t)NB;  // 0: longest; NB: no row
@@ -1012,13 +995,22 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
             chunk += c;
         }
         const uint32_t r0 = before + mine + mbcnt(mask[i]);
-        if (bk[i] == want && r0 == m) sm.total = (uint32_t)((int)threadIdx.x + i * NT);
+        if (bk[i] == want && r0 == m) {
+            sm.total = (uint32_t)((int)threadIdx.x + i * NT);
+            sm.win_base = wb[i];
+            sm.win_n = wn[i];
+        }
         before += chunk;
     }
     lds_sync();
     const int row = (int)sm.total;
+    base = sm.win_base;
+    n = sm.win_n;
     lds_sync();  // sm.total is rewritten later
-    return (row >= 0 && row < p.num_rows) ? row : (int)(bid % (uint32_t)p.num_rows);
+    if (row >= 0 && row < p.num_rows) return row;
+    const int r = (int)(bid % (uint32_t)p.num_rows);  // not reached: the map is a bijection
+    Policy::window(p, r, base, n);
+    return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,11 +1027,23 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const uint32_t bid = blockIdx.x;
     const uint32_t unit = (bid & 7u) * (uint32_t)p.units_per_xcd + (bid >> 3);
     if (unit >= (uint32_t)p.num_units) return;
-    const int r = p.balance ? balanced_row<Policy>(sm, p, bid) : (int)(unit / (uint32_t)p.nsplit);
-    const int c = p.balance ? 0 : (int)(unit - (uint32_t)r * (uint32_t)p.nsplit);
-
+    // The row and its window are the same in every lane, but they arrive
+    // through LDS and vector loads; readfirstlane puts them in scalar
+    // registers, so the stream's buffer offsets are scalar and its loads need
+    // no per-lane loop.
     int64_t base, n;
-    Policy::window(p, r, base, n);
+    int r;
+    if (p.balance) {
+        r = balanced_row<Policy>(sm, p, bid, base, n);
+    } else {
+        r = (int)(unit / (uint32_t)p.nsplit);
+        Policy::window(p, r, base, n);
+    }
+    r = __builtin_amdgcn_readfirstlane(r);
+    const int c = p.balance ? 0 : (int)(unit - (uint32_t)r * (uint32_t)p.nsplit);
+    // window starts and lengths lie in [0, width], width < 2^31
+    base = __builtin_amdgcn_readfirstlane((int)base);
+    n = __builtin_amdgcn_readfirstlane((int)n);
     const raw_t* row = static_cast<const raw_t*>(p.x) + (int64_t)r * p.row_stride + base;
     if (n <= p.k) {
         if (c == 0) short_row<DT, Policy>(p, r, base, n, row);
@@ -1054,7 +1058,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const Slice s = make_slice<DT>(row, n, c, eff);
     uint32_t* gkey = p.ws_key + (size_t)unit * WSCAP;
     uint32_t* gidx = p.ws_idx + (size_t)unit * WSCAP;
-    const Buf B{gkey, gidx, (uint32_t)p.lds_cap, (uint32_t)p.hi_cap, (uint32_t)p.lo_cap};
+    const Buf B{gkey, gidx, (uint32_t)p.lds_cap, (uint32_t)p.hi_cap};
     // body vectors of this unit, relative indexing (32-bit)
     const u32x4* vb = reinterpret_cast<const u32x4*>(row + s.h) + s.v0;
     const uint32_t nvec = (uint32_t)(s.v1 - s.v0);
@@ -1079,14 +1083,14 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     load_step(RA, rs, order.first(0, STEP));
     if (threadIdx.x == 0) {
         sm.cand_n = 0;
-        sm.lo_n = 0;
+        sm.up_n = 0;
     }
     hist_clear(sm);    // every select leaves the histogram zeroed again
     spread_clear(sm);  // the sample select's first-pass copies
     lds_sync();        // the loads stay in flight
     const Rungs G = sample_rungs<DT>(sm, p, n, S);
 
-    uint32_t nh, nl, lcap;  // upper / lower candidates, on-chip part of the upper ones
+    uint32_t nh, nup;  // candidates (keys >= T), of which keys >= T2
     if (!refiltered) {
         filter_scalars<DT>(sm, B, row, s.s0, s.s1, G);
         constexpr uint32_t SIGN = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
@@ -1099,10 +1103,10 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         filter_scalars<DT>(sm, B, row, s.t0, s.t1, G);
         __syncthreads();  // also completes the workspace stores of every thread
         nh = sm.cand_n;
-        nl = sm.lo_n;
+        nup = sm.up_n;
         hist_clear(sm);  // the staging queues overlaid the histogram
         lds_sync();      // everyone has read the counts before they can change
-        if (nh > B.hi_cap || nl > B.lo_cap) {  // slots ran out: re-filter with compaction
+        if (nh > B.hi_cap) {  // slots ran out: re-filter with compaction
             if (threadIdx.x == 0) gatomic_add(p.ws_stats + 0, 1u);
             refiltered = true;
         }
@@ -1111,38 +1115,39 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         careful_filter<DT>(sm, p, row, s, Thr{G.T, false});
         __syncthreads();
         nh = sm.cand_n;  // every candidate is on chip now
-        nl = 0;
+        nup = 0;
         __syncthreads();
     }
-    lcap = refiltered ? (uint32_t)CAP : B.lds_cap;
+    const uint32_t lcap = refiltered ? (uint32_t)CAP : B.lds_cap;
     const uint32_t own = nh < lcap ? nh : lcap;
+    // rank the keys >= T2 when at least k of them exist, else the whole list
+    // (a re-filtered list has no T2 count: all of it)
+    const bool whole_list = refiltered;
+    const bool upper = !whole_list && nup >= (uint32_t)p.k;
 
     if (eff == 1) {
-        if (nh + nl < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
-            if (threadIdx.x == 0 && nh + nl < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
+        if (nh < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
+            if (threadIdx.x == 0 && nh < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
             __syncthreads();
             whole_row<DT, Policy>(sm, p, r, base, n, row);
             return;
         }
-        const bool need_lo = nh < (uint32_t)p.k;
-        if (!need_lo && nh > own && nh <= (uint32_t)(LdsSrc::J * NT)) {
-            // a small spill: select over the on-chip and the spilled slots as they are
-            if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
-            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, own, gkey, gidx, nh));
+        if (threadIdx.x == 0 && !upper && !whole_list) gatomic_add(p.ws_stats + 3, 1u);
+        const uint32_t thr = upper ? G.T2 : 0u;
+        if (nh <= (uint32_t)(LdsSrc::J * NT)) {
+            // the on-chip slots and any spilled ones, selected as they are
+            if (threadIdx.x == 0 && nh > own) gatomic_add(p.ws_stats + 2, 1u);
+            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, own, gkey, gidx, nh, thr));
             return;
         }
-        if (nh > own || need_lo) {  // pull spilled / lower-rung candidates into LDS
-            if (threadIdx.x == 0) {
-                sm.cand_n = own;
-                if (nh > own) gatomic_add(p.ws_stats + 2, 1u);
-                if (need_lo) gatomic_add(p.ws_stats + 3, 1u);
-            }
-            __syncthreads();
-            Thr thr{G.T, false};
-            if (nh > own) ingest_global<DT>(sm, p.k, gkey + own, gidx + own, nh - own, thr);
-            if (need_lo)
-                ingest_global<DT>(sm, p.k, gkey + HI_SLOTS, gidx + HI_SLOTS, nl, thr);
+        // a long spill: pull it into LDS with the compaction filter
+        if (threadIdx.x == 0) {
+            sm.cand_n = own;
+            gatomic_add(p.ws_stats + 2, 1u);
         }
+        __syncthreads();
+        Thr th{upper ? G.T2 : G.T, false};
+        ingest_global<DT>(sm, p.k, gkey + own, gidx + own, nh - own, th);
         __syncthreads();
         const uint32_t m = sm.cand_n;
         __syncthreads();
@@ -1156,11 +1161,10 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         gstore(gidx + q, sm.idx[q]);
     }
     if (threadIdx.x == 0) {
-        // a re-filtered unit keeps every key >= T (or its chunk's top k) on the
-        // upper list without separating the rungs: the flag makes the merge
-        // read every lower list too
+        // a re-filtered unit's list holds its chunk's top k (or every key >=
+        // T) with no T2 count: the flag makes the merge rank every list whole
         gstore(p.ws_count + unit, nh);
-        gstore(p.ws_count_lo + unit, nl | (refiltered ? 0x80000000u : 0u));
+        gstore(p.ws_count_up + unit, nup | (whole_list ? 0x80000000u : 0u));
     }
     // Hand-off: the barrier orders every thread's candidate stores before
     // thread 0's agent-scope release fence, which precedes the ticket; the
@@ -1183,50 +1187,46 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const uint32_t unit0 = (uint32_t)r * (uint32_t)p.nsplit;
     if (threadIdx.x < (unsigned)eff) {
         sm.seg_hi[threadIdx.x] = gload(p.ws_count + unit0 + threadIdx.x);
-        sm.seg_lo[threadIdx.x] = gload(p.ws_count_lo + unit0 + threadIdx.x);
+        sm.seg_lo[threadIdx.x] = gload(p.ws_count_up + unit0 + threadIdx.x);
     }
     if (threadIdx.x == 0) gstore(p.ws_ticket + r, 0u);  // self-restoring
     __syncthreads();
-    uint32_t th = 0, tl = 0;
+    uint32_t th = 0, tup = 0;
     bool mixed = false;  // some unit was re-filtered
     for (int q = 0; q < eff; ++q) {
         th += sm.seg_hi[q];
-        tl += sm.seg_lo[q] & 0x7FFFFFFFu;
+        tup += sm.seg_lo[q] & 0x7FFFFFFFu;
         mixed |= (sm.seg_lo[q] >> 31) != 0;
     }
-    if (th + tl < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
-        if (threadIdx.x == 0 && th + tl < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
+    if (th < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
+        if (threadIdx.x == 0 && th < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
         __syncthreads();
         whole_row<DT, Policy>(sm, p, r, base, n, row);
         return;
     }
-    const bool need_lo = th < (uint32_t)p.k || mixed;
+    const bool rupper = !mixed && tup >= (uint32_t)p.k;
     // This unit's on-chip candidates stay in place; the other units' (and this
     // unit's spilled ones) are pulled in with the compaction filter.
     if (threadIdx.x == 0) {
         sm.cand_n = own;
         if (th > (uint32_t)CAP) gatomic_add(p.ws_stats + 2, 1u);
-        if (need_lo) gatomic_add(p.ws_stats + 3, 1u);
+        if (!rupper) gatomic_add(p.ws_stats + 3, 1u);
     }
     __syncthreads();
     const uint32_t* rkey = p.ws_key + (size_t)unit0 * WSCAP;
     const uint32_t* ridx = p.ws_idx + (size_t)unit0 * WSCAP;
-    Thr thr{G.T, false};
+    Thr thr{rupper ? G.T2 : G.T, false};
     for (int q = 0; q < eff; ++q) {
         const uint32_t mq = sm.seg_hi[q];
         const uint32_t from = q == c ? own : 0u;
         if (mq > from)
             ingest_global<DT>(sm, p.k, rkey + (size_t)q * WSCAP + from,
                               ridx + (size_t)q * WSCAP + from, mq - from, thr);
-        const uint32_t lq = sm.seg_lo[q] & 0x7FFFFFFFu;
-        if (need_lo && lq > 0)
-            ingest_global<DT>(sm, p.k, rkey + (size_t)q * WSCAP + HI_SLOTS,
-                              ridx + (size_t)q * WSCAP + HI_SLOTS, lq, thr);
     }
     __syncthreads();
     const uint32_t m = sm.cand_n;
     __syncthreads();
-    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, m));
+    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, m, rupper ? G.T2 : 0u));
 }
 
 // ---------------------------------------------------------------------------
