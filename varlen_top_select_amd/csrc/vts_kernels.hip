@@ -836,14 +836,20 @@ struct LdsSrc {
     __device__ __forceinline__ LdsSrc(Smem& sm, uint32_t own, const uint32_t* gkey,
                                       const uint32_t* gidx, uint32_t n_, uint32_t thr_)
         : n(n_), thr(thr_) {
+        // every load of both parts is issued before any is used; only the
+        // spilled slots [own, n) are read from the workspace
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const uint32_t q = (uint32_t)j * NT + threadIdx.x;
-            const uint32_t ql = q < own ? q : 0u, qg = q < n ? q : 0u;
-            const uint32_t kl = sm.key[ql], il = sm.idx[ql];
-            const uint32_t kg = gload(gkey + qg), ig = gload(gidx + qg);
-            key[j] = q < own ? kl : (q < n ? kg : 0u);
-            idx[j] = q < own ? il : (q < n ? ig : 0u);
+            key[j] = 0u;
+            idx[j] = 0u;
+            if (q < own) {
+                key[j] = sm.key[q];
+                idx[j] = sm.idx[q];
+            } else if (q < n) {
+                key[j] = gload(gkey + q);
+                idx[j] = gload(gidx + q);
+            }
         }
     }
     template <class F>
@@ -1134,9 +1140,13 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         }
         if (threadIdx.x == 0 && !upper && !whole_list) gatomic_add(p.ws_stats + 3, 1u);
         const uint32_t thr = upper ? G.T2 : 0u;
+        if (nh <= own) {  // every candidate on chip: the usual case
+            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, nh, thr));
+            return;
+        }
         if (nh <= (uint32_t)(LdsSrc::J * NT)) {
-            // the on-chip slots and any spilled ones, selected as they are
-            if (threadIdx.x == 0 && nh > own) gatomic_add(p.ws_stats + 2, 1u);
+            // the on-chip slots and the spilled ones, selected as they are
+            if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
             select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, own, gkey, gidx, nh, thr));
             return;
         }
@@ -1205,16 +1215,62 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         return;
     }
     const bool rupper = !mixed && tup >= (uint32_t)p.k;
-    // This unit's on-chip candidates stay in place; the other units' (and this
-    // unit's spilled ones) are pulled in with the compaction filter.
+    const uint32_t* rkey = p.ws_key + (size_t)unit0 * WSCAP;
+    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * WSCAP;
     if (threadIdx.x == 0) {
-        sm.cand_n = own;
         if (th > (uint32_t)CAP) gatomic_add(p.ws_stats + 2, 1u);
         if (!rupper) gatomic_add(p.ws_stats + 3, 1u);
     }
+    if (th <= (uint32_t)CAP) {
+        // Every list fits on chip: this unit's candidates stay in LDS slots
+        // [0, own); the rest -- the other units' lists and this unit's spill,
+        // m entries in all -- are gathered behind them in one pass, eight
+        // entries per thread per round with all their loads in flight, and
+        // the row is selected directly.  seg_lo now holds each list's first
+        // gathered slot.
+        const uint32_t m = th - own;
+        __syncthreads();  // every thread has read the counts in seg_lo
+        if (threadIdx.x == 0) {
+            uint32_t acc = 0;
+            for (int q = 0; q < eff; ++q) {
+                sm.seg_lo[q] = acc;
+                acc += sm.seg_hi[q] - (q == c ? own : 0u);
+            }
+        }
+        __syncthreads();
+        constexpr int E = 8;
+        for (uint32_t b0 = 0; b0 < m; b0 += (uint32_t)NT * E) {
+            uint32_t kk[E], cc[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t i = b0 + (uint32_t)e * NT + threadIdx.x;
+                kk[e] = 0u;
+                cc[e] = 0u;
+                if (i < m) {
+                    int q = 0;  // the list holding gathered entry i
+                    while (q + 1 < eff && sm.seg_lo[q + 1] <= i) ++q;
+                    const size_t at = (size_t)q * WSCAP + (i - sm.seg_lo[q]) + (q == c ? own : 0u);
+                    kk[e] = gload(rkey + at);
+                    cc[e] = gload(ridx + at);
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const uint32_t i = b0 + (uint32_t)e * NT + threadIdx.x;
+                if (i < m) {
+                    sm.key[own + i] = kk[e];
+                    sm.idx[own + i] = cc[e];
+                }
+            }
+        }
+        __syncthreads();
+        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, th, rupper ? G.T2 : 0u));
+        return;
+    }
+    // Too many for the on-chip slots: this unit's candidates stay in place and
+    // the others are pulled in with the compaction filter.
+    if (threadIdx.x == 0) sm.cand_n = own;
     __syncthreads();
-    const uint32_t* rkey = p.ws_key + (size_t)unit0 * WSCAP;
-    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * WSCAP;
     Thr thr{rupper ? G.T2 : G.T, false};
     for (int q = 0; q < eff; ++q) {
         const uint32_t mq = sm.seg_hi[q];
