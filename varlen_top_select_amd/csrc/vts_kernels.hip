@@ -297,9 +297,13 @@ __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* ro
     }
 }
 
-template <int DT>
+// `after_keys` runs once the sampled keys are in registers (the sample loads
+// have landed) and before the selection: the caller issues its first
+// streaming loads there, so that they neither delay the sample's arrival
+// nor wait for the selection.
+template <int DT, class AfterKeys>
 __device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t n,
-                                              Sample<DT>& S) {
+                                              Sample<DT>& S, AfterKeys after_keys) {
     constexpr int BITS = Traits<DT>::BITS;
     constexpr int VE = Traits<DT>::VE;
     uint32_t q = (uint32_t)p.k, q2 = q;
@@ -315,6 +319,11 @@ __device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
         key[j] = to_key<DT>((typename Traits<DT>::raw_t)vec_elem<DT>(S.v[j / VE], j % VE));
+    // the keys exist before anything after this point (the clobber also keeps
+    // the caller's loads from being hoisted above it)
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) __asm__ volatile("" ::"v"(key[j]) : "memory");
+    after_keys();
     auto visit = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < SPT; ++j)
@@ -969,16 +978,17 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     const uint32_t g = x * BALANCE_CUS_PER_XCD + k % BALANCE_CUS_PER_XCD;
     const uint32_t j = k / BALANCE_CUS_PER_XCD;
     const uint32_t rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
-    // bucket holding the rank and the rank within it (the same in every thread)
-    uint32_t acc = 0, want = NB, m = 0;
-    for (int b = 0; b < NB; ++b) {
-        const uint32_t c = cnt[b];
-        if (want == NB && rank < acc + c) {
-            want = (uint32_t)b;
-            m = rank - acc;
-        }
-        acc += c;
-    }
+    // bucket holding the rank and the rank within it (the same in every
+    // thread): lane b scans bucket b's count, the first lane whose running
+    // total passes the rank names it
+    static_assert(NB <= 64, "one bucket per lane");
+    const uint32_t lb = lane_id();
+    const uint32_t cb = lb < (uint32_t)NB ? cnt[lb] : 0u;
+    const uint32_t incl = wave_scan(cb, 0u, OpAdd());
+    const uint64_t past = ballot(lb < (uint32_t)NB && incl > rank);
+    const uint32_t want = past ? (uint32_t)__builtin_ctzll(past) : (uint32_t)NB;
+    const uint32_t m =
+        past ? rank - (uint32_t)__builtin_amdgcn_readlane((int)(incl - cb), (int)want) : 0u;
     // The m-th row of that bucket in row order; row i * NT + t is thread t's
     // bk[i].  One ballot per chunk i, all counts published at once.
     const uint32_t w = threadIdx.x >> 6;
@@ -1071,8 +1081,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const uint32_t col0 = (uint32_t)(s.h + s.v0 * Traits<DT>::VE);
     constexpr int U = Traits<DT>::U;
 
-    // The sample's loads go out first, then the first streaming step's, which
-    // stay in flight while the rungs are computed.
+    // The sample's loads go out first; the first streaming step's follow once
+    // the sample has landed and stay in flight while the rungs are computed.
     Sample<DT> S;
     sample_load<DT>(row, n, spread_hash((uint32_t)r), S);
     u32x4 RA[U], RB[U];
@@ -1086,7 +1096,6 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     order.rot = order.nsteps > 1
                     ? (uint32_t)(((uint64_t)spread_hash(unit) * order.nsteps) >> 32)
                     : 0u;
-    load_step(RA, rs, order.first(0, STEP));
     if (threadIdx.x == 0) {
         sm.cand_n = 0;
         sm.up_n = 0;
@@ -1094,7 +1103,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     hist_clear(sm);    // every select leaves the histogram zeroed again
     spread_clear(sm);  // the sample select's first-pass copies
     lds_sync();        // the loads stay in flight
-    const Rungs G = sample_rungs<DT>(sm, p, n, S);
+    const Rungs G =
+        sample_rungs<DT>(sm, p, n, S, [&]() { load_step(RA, rs, order.first(0, STEP)); });
 
     uint32_t nh, nup;  // candidates (keys >= T), of which keys >= T2
     if (!refiltered) {
