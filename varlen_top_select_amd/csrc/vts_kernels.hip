@@ -822,14 +822,18 @@ __device__ __forceinline__ void ingest_global(Smem& sm, int k, const uint32_t* g
 // final selection and epilogue
 // ---------------------------------------------------------------------------
 
+// registers per thread that hold every on-chip candidate slot
+constexpr int ONCHIP_J = (CAP + NT - 1) / NT;
+
 // Enumerates candidate entries (key, col) with wave-uniform trip counts.
 // The first `own` entries come from LDS slots [0, own), the rest, up to n,
 // from slots [own, n) of a workspace list (a unit's spilled candidates); all
 // are read once into registers (entry j * NT + threadIdx.x in register j), so
 // the selection passes and the emission visit registers.  Only keys >= thr
-// are visited.  n <= J * NT.
+// are visited.  n <= J * NT: J = 15 covers the on-chip slots, the default
+// J = 20 a list with up to 5120 entries.
+template <int J = 20>
 struct LdsSrc {
-    static constexpr int J = 20;
     static_assert(J * NT >= CAP, "every on-chip slot has a register");
     uint32_t n, thr;
     uint32_t key[J], idx[J];
@@ -927,7 +931,7 @@ __device__ __forceinline__ void whole_row(Smem& sm, const Params& p, int r, int6
     __syncthreads();
     const uint32_t cand = sm.cand_n;
     __syncthreads();
-    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, cand));
+    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc<ONCHIP_J>(sm, cand));
 }
 
 // Length-balanced placement of rows (one workgroup per row, R = 256 * s rows,
@@ -1151,13 +1155,13 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         if (threadIdx.x == 0 && !upper && !whole_list) gatomic_add(p.ws_stats + 3, 1u);
         const uint32_t thr = upper ? G.T2 : 0u;
         if (nh <= own) {  // every candidate on chip: the usual case
-            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, nh, thr));
+            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc<ONCHIP_J>(sm, nh, thr));
             return;
         }
-        if (nh <= (uint32_t)(LdsSrc::J * NT)) {
+        if (nh <= (uint32_t)(20 * NT)) {
             // the on-chip slots and the spilled ones, selected as they are
             if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
-            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, own, gkey, gidx, nh, thr));
+            select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc<20>(sm, own, gkey, gidx, nh, thr));
             return;
         }
         // a long spill: pull it into LDS with the compaction filter
@@ -1171,7 +1175,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         __syncthreads();
         const uint32_t m = sm.cand_n;
         __syncthreads();
-        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, m));
+        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc<ONCHIP_J>(sm, m));
         return;
     }
 
@@ -1274,7 +1278,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
             }
         }
         __syncthreads();
-        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, th, rupper ? G.T2 : 0u));
+        select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc<ONCHIP_J>(sm, th, rupper ? G.T2 : 0u));
         return;
     }
     // Too many for the on-chip slots: this unit's candidates stay in place and
@@ -1292,7 +1296,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     __syncthreads();
     const uint32_t m = sm.cand_n;
     __syncthreads();
-    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc(sm, m, rupper ? G.T2 : 0u));
+    select_and_emit<DT, Policy>(sm, p, r, base, LdsSrc<ONCHIP_J>(sm, m, rupper ? G.T2 : 0u));
 }
 
 // ---------------------------------------------------------------------------
