@@ -324,12 +324,43 @@ __device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t
 #pragma unroll
     for (int j = 0; j < SPT; ++j) __asm__ volatile("" ::"v"(key[j]) : "memory");
     after_keys();
+    Rungs R;
+    if (!S.whole && q <= (uint32_t)NT) {
+        // Every sampled key is valid here (vmask is full).  Each thread keeps
+        // its four largest keys and the rungs are ranked among those 4 * NT:
+        // the result is the sample's own order statistic unless one thread
+        // holds more than four of the sample's top q keys, and a lower bound
+        // of it otherwise -- a lower rung only admits more candidates, so the
+        // rungs stay safe -- with an eighth of the histogram atomics.
+        uint32_t t0 = 0, t1 = 0, t2 = 0, t3 = 0;
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            uint32_t x = key[j], hi;
+            hi = x > t0 ? x : t0;
+            x = x > t0 ? t0 : x;
+            t0 = hi;
+            hi = x > t1 ? x : t1;
+            x = x > t1 ? t1 : x;
+            t1 = hi;
+            hi = x > t2 ? x : t2;
+            x = x > t2 ? t2 : x;
+            t2 = hi;
+            t3 = x > t3 ? x : t3;
+        }
+        auto visit4 = [&](auto f) {
+            f(t0);
+            f(t1);
+            f(t2);
+            f(t3);
+        };
+        block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(sm, visit4, q, q2, R.T, R.T2);
+        return R;
+    }
     auto visit = [&](auto f) {
 #pragma unroll
         for (int j = 0; j < SPT; ++j)
             if ((S.vmask >> j) & 1u) f(key[j]);
     };
-    Rungs R;
     block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(sm, visit, q, q2, R.T, R.T2);
     return R;
 }
