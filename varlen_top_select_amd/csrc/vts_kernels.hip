@@ -276,8 +276,12 @@ __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* ro
     // rows are shorter than 2^31 bytes, so the grid fits a 32-bit range
     const uint32_t nv = (uint32_t)(((uint64_t)n + mis + VE - 1) / VE);
     const __amdgpu_buffer_rsrc_t rs = body_rsrc(grid, nv * 16u);
-    // block starts in [0, span); a block ends by column n - 2 after rounding up
-    const uint64_t span = whole ? 0u : (uint64_t)(n - SAMPLE_BLOCK - (VE - 1));
+    // A block starts on a 128-byte line (its grid vector index is congruent
+    // to lead mod 8), so its 256 bytes are exactly two cache lines; rounding
+    // up moves it at most VE - 1 + 7 * VE columns past its nominal column.
+    // Block starts lie in [0, span), so every block ends by column n - 1.
+    const uint32_t lead = (8u - (uint32_t)(((uintptr_t)grid >> 4) & 7u)) & 7u;
+    const uint64_t span = whole ? 0u : (uint64_t)(n - SAMPLE_BLOCK - (VE - 1) - 7 * VE);
     const uint64_t shift = (salt * span) >> 32;
     S.whole = whole;
     S.vmask = 0;
@@ -286,7 +290,9 @@ __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* ro
         const uint32_t g = threadIdx.x + (uint32_t)j * NT;  // 0 .. SAMPLE / VE - 1
         const uint64_t b = g / VPB;
         const uint32_t c = (uint32_t)((b * span + shift) / SAMPLE_BLOCKS);
-        const uint32_t gv = whole ? g : (c + mis + VE - 1) / VE + g % VPB;
+        const uint32_t g0 = (c + mis + VE - 1) / VE;   // first grid vector at or after c
+        const uint32_t gl = g0 + ((lead - g0) & 7u);   // ... on a 128-byte line
+        const uint32_t gv = whole ? g : gl + g % VPB;
         S.v[j] = __builtin_bit_cast(
             u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(gv * 16u), 0, 0));
 #pragma unroll
@@ -620,9 +626,13 @@ __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (
 // batch read different address ranges of their rows instead of all reading
 // the same offset of equally spaced rows, which would load a few HBM channels
 // and leave the rest idle.
+// A step s >= nsteps (the loop's last prefetch) maps past the unit's body,
+// where the buffer's range check answers every load with zeros without a
+// memory access.
 struct StepOrder {
     uint32_t nsteps, rot;
     __device__ __forceinline__ uint32_t first(uint32_t s, uint32_t step) const {
+        if (s >= nsteps) return nsteps * step;
         uint32_t t = s + rot;
         if (t >= nsteps) t -= nsteps;
         return t * step;
@@ -656,8 +666,9 @@ __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[
     // On entry the loads of the first step (RA) are in flight.  The first step
     // is filtered before the loop, so on entry and on the back edge alike
     // exactly the loads of RB are in flight at the loop header: the compiler's
-    // wait counts then let them stay in flight while RA is filtered.  (A load
-    // for a step past the last one re-reads an earlier step: harmless.)
+    // wait counts then let them stay in flight while RA is filtered.  (The
+    // loads for the step past the last one fall outside the buffer: zeros,
+    // no memory traffic.)
     const uint32_t ns = order.nsteps;
     load_step(RB, rs, order.first(1, STEP));
     step(RA, order.first(0, STEP));
