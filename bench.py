@@ -3,7 +3,7 @@
 Default workload: the long-row decode batch -- 1024 rows x 262144 fp32 logits,
 top_k 2048, seq_lens U[131072, 262144] with 5 % of rows longer than the width
 (clamped), spiky N(0,1) values, previous-step hint (workloads/synth.py,
-config 3).  One step = one topk_varlen call over the whole batch (prologue,
+"long").  One step = one topk_varlen call over the whole batch (prologue,
 sampled threshold, streaming filter, selection, epilogue: the entire path).
 
 Prints ONE JSON line:
@@ -231,7 +231,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--workload", default="long",
+                    choices=["small", "dsv32", "long", "dsv4_mtp", "page"])
     ap.add_argument("--no-hint", action="store_true")
     ap.add_argument("--cold-reps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true")
@@ -245,7 +246,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this selection path runs on a single MI355X; "
-              "rows are independent, so a multi-GPU run would shard rows (see DESIGN.md).",
+              "rows are independent, so a multi-GPU run would shard them by rows (balanced by "
+              "valid length) with no exchange between GPUs.",
               file=sys.stderr)
         return 2
 
@@ -255,8 +257,8 @@ def main() -> int:
     import workloads
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    log(f"generating config {args.config}")
-    wl = workloads.make(args.config, hint=not args.no_hint)
+    log(f"generating workload {args.workload}")
+    wl = workloads.make(args.workload, hint=not args.no_hint)
     n = valid_lengths(wl)
     isz = 4 if wl.dtype == 0 else 2
     valid = int(n.sum()) * isz
@@ -301,7 +303,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": {0: "f32", 1: "bf16", 2: "f16"}[wl.dtype],
         "data": "synthetic",
-        "config": {"workload": f"config {args.config} ({wl.name}): {wl.rows}x{wl.width} "
+        "config": {"workload": f"{wl.name}: {wl.rows}x{wl.width} "
                                f"{ {0: 'fp32', 1: 'bf16', 2: 'fp16'}[wl.dtype]}, top_k {wl.k}",
                    "rows": wl.rows, "width": wl.width, "top_k": wl.k,
                    "hint": (not args.no_hint) and wl.pre_idx is not None,
@@ -350,18 +352,18 @@ def main() -> int:
 
     if not args.no_others:
         others = {}
-        for c in (1, 2, 4, 5):
-            if c == args.config:
+        for name in ("small", "dsv32", "long", "dsv4_mtp", "page"):
+            if name == args.workload:
                 continue
-            log(f"config {c}")
-            w2 = workloads.make(c)
+            log(f"workload {name}")
+            w2 = workloads.make(name)
             n2 = valid_lengths(w2)
             s2, ws2 = make_step(w2, torch, vts)
             for _ in range(5):
                 s2()
             ct2 = cold_times(s2, torch, 20)
             vb2 = int(n2.sum()) * (4 if w2.dtype == 0 else 2)
-            others[f"config{c}_{w2.name}"] = {
+            others[w2.name] = {
                 "us_median_cold": round(float(np.median(ct2)), 2),
                 "valid_GBps": round(vb2 / (np.median(ct2) * 1e-6) / 1e9, 1),
                 "valid_bytes": vb2}

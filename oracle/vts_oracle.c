@@ -33,7 +33,7 @@
  *                  both outputs.  `lengths`/`row_starts` follow the SGLang
  *                  TopK_Ops page, I/O contract of fast_topk_v2.
  *
- * Readings taken where the pages are silent (each also listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - equal values (including -0 and +0) are ties; the oracle breaks them by
  *     ascending column so its own output is deterministic;
  *   - NaN: the pages call its order implementation specific.  The oracle puts a

@@ -29,25 +29,25 @@ def _assert_ok(errs):
 # the five workloads at full size, in the launch configuration the bench times
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_varlen_config_full(cfg):
-    wl = workloads.make(cfg)
-    say(f"config {cfg} full {wl.x.shape} k={wl.k} hint={wl.pre_idx is not None}")
+@pytest.mark.parametrize("name", ["small", "dsv32", "long", "dsv4_mtp"])
+def test_varlen_workload_full(name):
+    wl = workloads.make(name)
+    say(f"{name} full {wl.x.shape} k={wl.k} hint={wl.pre_idx is not None}")
     idx, vals, stats = run_varlen(wl)
-    say(f"config {cfg} stats {stats}")
+    say(f"{name} stats {stats}")
     _assert_ok(check_varlen(wl, idx, vals))
 
 
-def test_varlen_config3_hint_free():
-    wl = workloads.make(3, hint=False)
-    say("config 3 full, hint-free")
+def test_varlen_long_hint_free():
+    wl = workloads.make("long", hint=False)
+    say("long full, hint-free")
     idx, vals, stats = run_varlen(wl)
     _assert_ok(check_varlen(wl, idx, vals))
 
 
-def test_transform_config5_full():
-    wl = workloads.make(5)
-    say(f"config 5 full {wl.x.shape}")
+def test_transform_page_full():
+    wl = workloads.make("page")
+    say(f"page full {wl.x.shape}")
     out, raw, stats = run_transform(wl)
     _assert_ok(check_transform_wl(wl, out, raw))
 
@@ -57,12 +57,13 @@ def test_transform_config5_full():
 # every row must be taken exactly once, with the placement on and off
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg,rows,width", [(3, 512, 16384), (3, 1024, 8192), (4, 768, 16384),
-                                            (5, 512, 8192), (3, 4096, 4096)])
+@pytest.mark.parametrize("name,rows,width", [("long", 512, 16384), ("long", 1024, 8192),
+                                             ("dsv4_mtp", 768, 16384),
+                                             ("page", 512, 8192), ("long", 4096, 4096)])
 @pytest.mark.parametrize("balance", [True, False])
-def test_balanced_placement(cfg, rows, width, balance):
-    wl = workloads.make(cfg, rows=rows, width=width)
-    say(f"config {cfg} rows {rows} width {width} balance {balance}")
+def test_balanced_placement(name, rows, width, balance):
+    wl = workloads.make(name, rows=rows, width=width)
+    say(f"{name} rows {rows} width {width} balance {balance}")
     with tuning(nsplit=1, no_balance=0 if balance else 1):
         if wl.kind == "varlen":
             idx, vals, stats = run_varlen(wl)
@@ -95,15 +96,15 @@ PATHS = {
     "split8_lo_overflow": dict(nsplit=8, min_chunk=1024, likely=1, spill=64),
 }
 
-REDUCED = {1: dict(rows=4), 2: dict(rows=8), 3: dict(rows=8, width=65536), 4: dict(rows=32),
-           5: dict(rows=24)}
+REDUCED = {"small": dict(rows=4), "dsv32": dict(rows=8), "long": dict(rows=8, width=65536),
+           "dsv4_mtp": dict(rows=32), "page": dict(rows=24)}
 
 
 @pytest.mark.parametrize("path", sorted(PATHS))
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
-def test_forced_paths(cfg, path):
-    wl = workloads.make(cfg, **REDUCED[cfg])
-    say(f"config {cfg} reduced {wl.x.shape} path {path}")
+@pytest.mark.parametrize("name", ["small", "dsv32", "long", "dsv4_mtp", "page"])
+def test_forced_paths(name, path):
+    wl = workloads.make(name, **REDUCED[name])
+    say(f"{name} reduced {wl.x.shape} path {path}")
     with tuning(**PATHS[path]):
         if wl.kind == "varlen":
             idx, vals, stats = run_varlen(wl)
@@ -137,7 +138,7 @@ def _varlen_wl(values_f32: np.ndarray, seq_lens, k, dtype=F32, next_n=1, cr=1, s
         bits = raw_bits
     x = np.zeros((R, S), bits.dtype)
     x[:, :W] = bits
-    return Workload(config=0, name="custom", kind="varlen", dtype=dtype, x=x, width=W, k=k,
+    return Workload(name="custom", kind="varlen", dtype=dtype, x=x, width=W, k=k,
                     seq_lens=np.asarray(seq_lens, np.int32), next_n=next_n, compress_ratio=cr,
                     pre_idx=pre_idx, return_values=return_values)
 
@@ -230,7 +231,7 @@ def test_mtp_grouping_and_compression(next_n, cr):
 
 
 def test_poisoned_columns_are_never_selected():
-    wl = workloads.make(2, rows=8)
+    wl = workloads.make("dsv32", rows=8)
     base, n = oracle.varlen_rows(wl.seq_lens, wl.rows, wl.next_n, wl.compress_ratio, wl.width)
     poison_outside(wl, base, n)
     say("poisoned columns")
@@ -239,7 +240,7 @@ def test_poisoned_columns_are_never_selected():
 
 
 def test_degenerate_hints():
-    wl = workloads.make(2, rows=8)
+    wl = workloads.make("dsv32", rows=8)
     R, k = wl.rows, wl.k
     for name, h in {
         "zeros": np.zeros((R, k), np.int32),
@@ -269,7 +270,7 @@ def test_nan_rows_do_not_crash_and_stay_valid():
 
 
 def test_repeat_calls_reuse_the_workspace():
-    wl = workloads.make(2, rows=16)
+    wl = workloads.make("dsv32", rows=16)
     x = torch.from_numpy(wl.x.view(np.float32)).cuda()
     seq = torch.from_numpy(wl.seq_lens).cuda()
     import varlen_top_select_amd as vts
@@ -288,7 +289,7 @@ def test_repeat_calls_reuse_the_workspace():
 # ---------------------------------------------------------------------------
 
 def test_transform_identity_page_size_1_no_starts():
-    wl = workloads.make(5, rows=16)
+    wl = workloads.make("page", rows=16)
     W = wl.width
     wl.page_size = 1
     wl.page_table = np.tile(np.arange(W + 8, dtype=np.int32), (wl.rows, 1))
@@ -302,14 +303,14 @@ def test_transform_identity_page_size_1_no_starts():
 
 
 def test_transform_without_raw_output():
-    wl = workloads.make(5, rows=8)
+    wl = workloads.make("page", rows=8)
     say("transform without out_raw")
     out, raw, _ = run_transform(wl, with_raw=False)
     _assert_ok(check_transform_wl(wl, out, None))
 
 
 def test_transform_odd_windows():
-    wl = workloads.make(5, rows=16)
+    wl = workloads.make("page", rows=16)
     W = wl.width
     wl.lengths[:] = np.array([0, -5, 1, 2047, 2048, 2049, W, W, 5, 3000, 70000, 40000, 7, 9,
                               100, 4096], np.int32)

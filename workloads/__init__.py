@@ -1,2 +1,2 @@
 """Seeded synthetic inputs shaped like the decode-step workloads (shared by tests, smoke, bench)."""
-from .synth import CONFIGS, Workload, make  # noqa: F401
+from .synth import WORKLOADS, Workload, make  # noqa: F401

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the five decode-step workloads.
+"""Seeded synthetic inputs for the five decode-step workloads, keyed by name.
 
 This module only draws random numbers and lays them out; it holds none of the
 selection arithmetic.  Both the HIP path and the CPU oracle take their inputs
@@ -8,23 +8,23 @@ Every row is drawn from its own child generator (numpy PCG64 seeded from
 ``SeedSequence(seed).spawn(rows)``), so any subset of rows can be rebuilt on
 its own and rows can be generated in parallel.  Shapes, laws and seeds:
 
-  1  "small"       fp32 [4, 4096], iid N(0,1); seq_lens ~ U{1..4096};
+  "small"          fp32 [4, 4096], iid N(0,1); seq_lens ~ U{1..4096};
                    top_k 512, next_n 1, compress_ratio 1, values returned.
-  2  "dsv32"       fp32 [64, 163840]; seq_lens ~ U{100000..163840}; each row is
+  "dsv32"          fp32 [64, 163840]; seq_lens ~ U{100000..163840}; each row is
                    N(0,1) with 1 % of its columns (drawn without replacement)
                    raised by U(2,6) ("spikes"); top_k 2048.  The previous-step
                    row P is drawn by the same law; the current row is P shifted
                    right by one column plus N(0, 0.1) noise (column 0 fresh).
                    pre_idx = the previous step's top-2048 of P over its valid
                    prefix (seq_len - 1), largest first.
-  3  "long"        fp32 [1024, 262144], the same spiky law and hint;
+  "long"           fp32 [1024, 262144], the same spiky law and hint;
                    95 % of seq_lens ~ U{131072..262144}, 5 % ~ U{262145..524288}
                    (longer than the width, so clamped).
-  4  "dsv4_mtp"    bf16 [512, 262144], next_n 2 (256 requests), compress_ratio 4,
+  "dsv4_mtp"       bf16 [512, 262144], next_n 2 (256 requests), compress_ratio 4,
                    seq_lens = floor(exp(U * ln(2^20 + 1))) in [1, 2^20] with at
                    least four requests forced to 1 (< next_n: empty rows);
                    top_k 1024; N(0,1) rounded to bf16 (nearest even).
-  5  "page"        fp16 [256, 65536] with row stride 65600; lengths ~ U{1..65536},
+  "page"           fp16 [256, 65536] with row stride 65600; lengths ~ U{1..65536},
                    at least 8 rows with length <= 2048; row_starts ~
                    U{0..65536 - length}; page_size 64; page table int32
                    [256, 1040] whose entries are disjoint random slices of one
@@ -32,8 +32,9 @@ its own and rows can be generated in parallel.  Shapes, laws and seeds:
                    page_table_row_starts ~ U{0..15}; top_k 2048.  Columns outside
                    a row's window hold the largest finite fp16 ("poisoned").
 
-Seeds: 20261200 + config number; the previous-step rows of configs 2 and 3 use
-that seed + 50.  The pre_idx of configs 2 and 3 is built with numpy's
+Seeds: 20261200 + the workload's seed offset (small 1, dsv32 2, long 3,
+dsv4_mtp 4, page 5); the previous-step rows of dsv32 and long use that seed
++ 50.  The pre_idx of dsv32 and long is built with numpy's
 partition and sort of the previous-step row: it is workload input (a
 previous step's answer), never an expected value, and the oracle does not read it.
 
@@ -54,17 +55,17 @@ import numpy as np
 F32, BF16, F16 = 0, 1, 2
 BASE_SEED = 20261200
 
-CONFIGS = {
-    1: dict(name="small", kind="varlen", dtype=F32, rows=4, width=4096, k=512, next_n=1, cr=1,
-            values=True, law="normal"),
-    2: dict(name="dsv32", kind="varlen", dtype=F32, rows=64, width=163840, k=2048, next_n=1, cr=1,
-            values=False, law="spiky"),
-    3: dict(name="long", kind="varlen", dtype=F32, rows=1024, width=262144, k=2048, next_n=1, cr=1,
-            values=False, law="spiky"),
-    4: dict(name="dsv4_mtp", kind="varlen", dtype=BF16, rows=512, width=262144, k=1024, next_n=2,
-            cr=4, values=False, law="normal"),
-    5: dict(name="page", kind="transform", dtype=F16, rows=256, width=65536, stride=65600, k=2048,
-            page_size=64, pt_cols=1040, law="normal"),
+WORKLOADS = {
+    "small": dict(seed_offset=1, kind="varlen", dtype=F32, rows=4, width=4096, k=512, next_n=1,
+                  cr=1, values=True, law="normal"),
+    "dsv32": dict(seed_offset=2, kind="varlen", dtype=F32, rows=64, width=163840, k=2048,
+                  next_n=1, cr=1, values=False, law="spiky"),
+    "long": dict(seed_offset=3, kind="varlen", dtype=F32, rows=1024, width=262144, k=2048,
+                 next_n=1, cr=1, values=False, law="spiky"),
+    "dsv4_mtp": dict(seed_offset=4, kind="varlen", dtype=BF16, rows=512, width=262144, k=1024,
+                     next_n=2, cr=4, values=False, law="normal"),
+    "page": dict(seed_offset=5, kind="transform", dtype=F16, rows=256, width=65536, stride=65600,
+                 k=2048, page_size=64, pt_cols=1040, law="normal"),
 }
 
 
@@ -72,7 +73,6 @@ CONFIGS = {
 class Workload:
     """One synthetic batch.  `x` holds raw element bits, shape [rows, row_stride]."""
 
-    config: int
     name: str
     kind: str  # "varlen" | "transform"
     dtype: int
@@ -141,18 +141,19 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def make(config: int, rows: int | None = None, seed: int | None = None, variant: str | None = None,
+def make(name: str, rows: int | None = None, seed: int | None = None, variant: str | None = None,
          width: int | None = None, hint: bool = True) -> Workload:
-    """Builds config `config` (1..5).  `rows`/`width` shrink it for quick cases."""
-    c = dict(CONFIGS[config])
+    """Builds the workload `name` (a key of WORKLOADS).  `rows`/`width` shrink it
+    for quick cases."""
+    c = dict(WORKLOADS[name])
     R = rows if rows is not None else c["rows"]
     W = width if width is not None else c["width"]
     S = c.get("stride", W) + (W - c["width"] if width is not None and "stride" in c else 0)
     S = max(S, W)
-    seed = BASE_SEED + config if seed is None else seed
+    seed = BASE_SEED + c["seed_offset"] if seed is None else seed
     g = np.random.default_rng(seed)
     k, dtype = c["k"], c["dtype"]
-    wl = Workload(config=config, name=c["name"], kind=c["kind"], dtype=dtype,
+    wl = Workload(name=name, kind=c["kind"], dtype=dtype,
                   x=np.empty((R, S), np.uint32 if dtype == F32 else np.uint16), width=W, k=k)
 
     # ---- lengths --------------------------------------------------------------
@@ -161,17 +162,17 @@ def make(config: int, rows: int | None = None, seed: int | None = None, variant:
         assert R % nn == 0
         nreq = R // nn
         wl.next_n, wl.compress_ratio, wl.return_values = nn, cr, c["values"]
-        if config == 1:
+        if name == "small":
             seq = g.integers(1, W + 1, size=nreq)
-        elif config == 2:
+        elif name == "dsv32":
             lo = max(1, int(W * 100000 / 163840))
             seq = g.integers(lo, W + 1, size=nreq)
-        elif config == 3:
+        elif name == "long":
             half = W // 2
             seq = g.integers(half, W + 1, size=nreq)
             longer = g.random(nreq) < 0.05
             seq[longer] = g.integers(W + 1, 2 * W + 1, size=int(longer.sum()))
-        else:  # config 4
+        else:  # dsv4_mtp
             top = 4 * W  # 2^20 at the full width
             u = g.random(nreq)
             seq = np.floor(np.exp(u * math.log(top + 1))).astype(np.int64)
@@ -199,7 +200,7 @@ def make(config: int, rows: int | None = None, seed: int | None = None, variant:
     want_hint = spiky and hint
     pre_idx = np.full((R // wl.next_n, k), -1, np.int32) if want_hint else None
     if want_hint:
-        # previous step: one token shorter (these configs have next_n = compress_ratio = 1)
+        # previous step: one token shorter (these workloads have next_n = compress_ratio = 1)
         assert wl.next_n == 1 and wl.compress_ratio == 1
         n_prev = np.clip(wl.seq_lens.astype(np.int64) - 1, 0, W)
 
