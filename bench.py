@@ -28,6 +28,7 @@ import ctypes
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -57,14 +58,22 @@ def valid_lengths(wl) -> np.ndarray:
     return np.clip(wl.lengths.astype(np.int64), 0, wl.width - start)
 
 
-def kernel_source_hash() -> str:
+def _code_only(text: str) -> str:
+    """Source text without comments and whitespace (a comment edit is not a kernel change)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r"\s+", "", text)
+
+
+def kernel_source_hash(csrc: str | None = None) -> str:
+    """Hash of the top-k library's code (comments and whitespace excluded)."""
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "varlen_top_select_amd", "csrc")
+    csrc = csrc or os.path.join(ROOT, "varlen_top_select_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
         if name.startswith("vts_probe"):
             continue
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -7,24 +7,25 @@
 //     top_k_varlen doc, `seq_lens`) or from lengths / row_starts (SGLang
 //     TopK_Ops, fast_topk_v2).  n == 0 and n <= k rows are answered directly
 //     (TensorRT-LLM PR #17821, short-row commit: identity then -1).
-//  2. thresholds: a fixed sample of the row (64 blocks of 64 contiguous
-//     columns, or the whole row when it is short) is radix-selected in LDS at
-//     two ranks -- a ladder of two rungs, after the sample-calibrated
-//     thresholds of the self-sampling GVR V2 description on the TensorRT-LLM
-//     PR #17821 page.  The safe rung T is placed so that, for exchangeable
-//     data, at least k row elements clear it except with negligible
-//     probability; the likely rung T2 >= T so that they clear it in most rows.
-//     All workgroups of a row compute the same rungs.
+//  2. thresholds: a fixed sample of the row (128 blocks of 64 contiguous
+//     columns, each on a cache line, or the whole row when it is short) is
+//     radix-selected in LDS at two ranks -- a ladder of two rungs, after the
+//     sample-calibrated thresholds of the self-sampling GVR V2 description on
+//     the TensorRT-LLM PR #17821 page.  The safe rung T is placed so that,
+//     for exchangeable data, at least k row elements clear it except with
+//     negligible probability; the likely rung T2 >= T so that they clear it
+//     in most rows.  All workgroups of a row compute the same rungs.
 //  3. filter: one coalesced pass over the unit's columns with 16-byte loads;
-//     keys >= T2 are appended to LDS and keys in [T, T2) to the workspace,
-//     both with one wave-aggregated ticket per wave and step.  If the slots
-//     run out, the unit is re-filtered with a compaction filter that keeps at
-//     most k candidates at any time (exact for any input, slower).
-//  4. verify: if at least k keys cleared T2, the top k are among them; else,
-//     if at least k cleared T, among those (the lower rung is read back);
-//     else the row is re-selected over all its columns with the compaction
-//     filter (never for exchangeable data: exactness rests on these counts,
-//     never on the sample).
+//     every key >= T is appended to one candidate list (LDS, then the unit's
+//     workspace region) with one wave-aggregated ticket per drained round of
+//     staged vectors, and the keys >= T2 are counted.  If the list outgrows
+//     its slots, the unit is re-filtered with a compaction filter that keeps
+//     at most k candidates at any time (exact for any input, slower).
+//  4. verify: if at least k keys cleared T2, the top k are among them and
+//     only those are ranked; else, if at least k cleared T, the whole list is
+//     ranked; else the row is re-selected over all its columns with the
+//     compaction filter (never for exchangeable data: exactness rests on
+//     these counts, never on the sample).
 //  5. select: the k-th largest candidate key K and the count g of keys > K,
 //     by radix select in LDS (10-bit digits from the first differing bit).
 //  6. epilogue: all keys > K and k - g keys == K are written (ties are
