@@ -1150,11 +1150,28 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     hist_clear(sm);    // every select leaves the histogram zeroed again
     spread_clear(sm);  // the sample select's first-pass copies
     lds_sync();        // the loads stay in flight
-    const Rungs G =
-        sample_rungs<DT>(sm, p, n, S, [&]() { load_step(RA, rs, order.first(0, STEP)); });
+    // A row that the sample read whole and that fits the on-chip candidate
+    // slots is selected directly: its first unit puts every column in the
+    // slot of its column (a second, cache-hot read of at most CAP elements)
+    // and selects from there -- no rungs, no stream; the row's other units,
+    // if any, have nothing to do.
+    const bool direct = S.whole && n <= (int64_t)B.lds_cap && p.force_path == FORCE_NONE;
+    if (direct) {
+        if (c != 0) return;
+        for (uint32_t col = threadIdx.x; col < (uint32_t)n; col += NT) {
+            sm.key[col] = to_key<DT>(gload(row + col));
+            sm.idx[col] = col;
+        }
+        __syncthreads();
+    }
+    Rungs G{0u, 0u};
+    if (!direct)
+        G = sample_rungs<DT>(sm, p, n, S, [&]() { load_step(RA, rs, order.first(0, STEP)); });
 
-    uint32_t nh, nup;  // candidates (keys >= T), of which keys >= T2
-    if (!refiltered) {
+    uint32_t nh = 0, nup = 0;  // candidates (keys >= T), of which keys >= T2
+    if (direct) {
+        nh = (uint32_t)n;  // every column, on chip
+    } else if (!refiltered) {
         filter_scalars<DT>(sm, B, row, s.s0, s.s1, G);
         constexpr uint32_t SIGN = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
         if (nvec == 0) {
@@ -1188,7 +1205,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const bool whole_list = refiltered;
     const bool upper = !whole_list && nup >= (uint32_t)p.k;
 
-    if (eff == 1) {
+    if (eff == 1 || direct) {  // one unit holds every candidate of the row
         if (nh < (uint32_t)p.k || p.force_path == FORCE_FALLBACK) {
             if (threadIdx.x == 0 && nh < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
             __syncthreads();
