@@ -65,13 +65,15 @@ def _code_only(text: str) -> str:
     return re.sub(r"\s+", "", text)
 
 
+KERNEL_SOURCES = ("vts_device.hpp", "vts_internal.h", "vts_kernels.hip")
+
+
 def kernel_source_hash(csrc: str | None = None) -> str:
-    """Hash of the top-k library's code (comments and whitespace excluded)."""
+    """Hash of the code that defines the top-k kernel (comments and whitespace
+    excluded; the host-side plan and argument checks are not part of it)."""
     h = hashlib.sha256()
     csrc = csrc or os.path.join(ROOT, "varlen_top_select_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.startswith("vts_probe"):
-            continue
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name)) as f:
             h.update(name.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]

@@ -13,10 +13,14 @@ namespace {
 
 using namespace vts;
 
-// Units of work per launch the plan aims for: four workgroups per compute unit
-// of an MI355X (256 CUs).  A fixed constant keeps the plan -- and the workspace
-// size -- independent of the device query.
-constexpr int64_t TARGET_UNITS = 4 * 256;
+// Units of work per launch the plan aims for: one workgroup per compute unit of
+// an MI355X (256 CUs).  Rows are split only while there are fewer rows than
+// that: every unit of a split row pays the sample and rung start and the row
+// pays a merge, which costs more than a partly idle launch (measured: 256 fp16
+// rows of 65536 run faster unsplit, 64 fp32 rows of 163840 fastest in four).
+// A fixed constant keeps the plan -- and the workspace size -- independent of
+// the device query.
+constexpr int64_t TARGET_UNITS = 256;
 // A row gets at most one workgroup per MIN_CHUNK valid columns: below about
 // 32K columns a split's fixed costs (its own sample and the merge) outweigh
 // the shorter stream (measured on the five benchmark shapes).
