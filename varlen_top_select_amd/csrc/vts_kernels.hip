@@ -304,6 +304,24 @@ __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* ro
     }
 }
 
+// The M largest of a thread's SPT keys, largest first (an insertion network of
+// max/min pairs; every key passes through all M places).
+template <int M>
+__device__ __forceinline__ void top_m(const uint32_t (&key)[SPT], uint32_t (&t)[M]) {
+#pragma unroll
+    for (int i = 0; i < M; ++i) t[i] = 0u;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+        uint32_t x = key[j];
+#pragma unroll
+        for (int i = 0; i < M; ++i) {
+            const uint32_t hi = x > t[i] ? x : t[i];
+            x = x > t[i] ? t[i] : x;
+            t[i] = hi;
+        }
+    }
+}
+
 // `after_keys` runs once the sampled keys are in registers (the sample loads
 // have landed) and before the selection: the caller issues its first
 // streaming loads there, so that they neither delay the sample's arrival
@@ -332,35 +350,30 @@ __device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t
     for (int j = 0; j < SPT; ++j) __asm__ volatile("" ::"v"(key[j]) : "memory");
     after_keys();
     Rungs R;
+    // Every sampled key is valid when the row is not read whole (vmask is
+    // full).  Then each thread may keep only its M largest keys and rank the
+    // rungs among those M * NT: the result is the sample's own order statistic
+    // unless one thread holds more than M of the sample's top q keys, and a
+    // lower bound of it otherwise -- a lower rung only admits more candidates,
+    // so the rungs stay safe -- with M / SPT of the histogram atomics.
     if (!S.whole && q <= (uint32_t)NT) {
-        // Every sampled key is valid here (vmask is full).  Each thread keeps
-        // its four largest keys and the rungs are ranked among those 4 * NT:
-        // the result is the sample's own order statistic unless one thread
-        // holds more than four of the sample's top q keys, and a lower bound
-        // of it otherwise -- a lower rung only admits more candidates, so the
-        // rungs stay safe -- with an eighth of the histogram atomics.
-        uint32_t t0 = 0, t1 = 0, t2 = 0, t3 = 0;
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            uint32_t x = key[j], hi;
-            hi = x > t0 ? x : t0;
-            x = x > t0 ? t0 : x;
-            t0 = hi;
-            hi = x > t1 ? x : t1;
-            x = x > t1 ? t1 : x;
-            t1 = hi;
-            hi = x > t2 ? x : t2;
-            x = x > t2 ? t2 : x;
-            t2 = hi;
-            t3 = x > t3 ? x : t3;
-        }
+        uint32_t t[4];
+        top_m<4>(key, t);
         auto visit4 = [&](auto f) {
-            f(t0);
-            f(t1);
-            f(t2);
-            f(t3);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) f(t[i]);
         };
         block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(sm, visit4, q, q2, R.T, R.T2);
+        return R;
+    }
+    if (!S.whole && q <= (uint32_t)(4 * NT)) {
+        uint32_t t[8];
+        top_m<8>(key, t);
+        auto visit8 = [&](auto f) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) f(t[i]);
+        };
+        block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(sm, visit8, q, q2, R.T, R.T2);
         return R;
     }
     auto visit = [&](auto f) {
