@@ -90,8 +90,8 @@ int vts_workspace_init(void* workspace, size_t bytes, void* stream);
  * next_n      >= 1, must divide num_rows.
  * compress_ratio >= 1.
  * pre_idx     device int32[num_rows / next_n, top_k] or NULL: the previous
- *             step's selection for each request, which the pages allow as a
- *             sampling anchor only.  It is validated (16-byte aligned, else
+ *             step's selection for each request, a sampling anchor only
+ *             (FlashInfer top_k_varlen doc, `pre_idx`).  It is validated (16-byte aligned, else
  *             ignored with VTS_WARN_HINT_DISCARDED) and never read by the
  *             current kernels, which estimate every threshold from a strided
  *             sample of the row.  Results never depend on it.
