@@ -85,7 +85,7 @@ def upload(wl, torch):
     return raw.view(dt)[:, : wl.width], dt
 
 
-def make_step(wl, torch, vts, hint: bool = True):
+def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False):
     """Returns (step, out tensors, workspace) for one call of the whole batch."""
     x, dt = upload(wl, torch)
     R, k = wl.rows, wl.k
@@ -103,6 +103,14 @@ def make_step(wl, torch, vts, hint: bool = True):
         return step, ws
     L = torch.from_numpy(wl.lengths).cuda()
     rs = torch.from_numpy(wl.row_starts).cuda()
+    if ragged:  # the same windows, each row's indices offset into a ragged KV buffer
+        off = torch.from_numpy((np.arange(R, dtype=np.int64) * wl.width).astype(np.int32)).cuda()
+        o = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        ws = vts.make_workspace(R, wl.width, k, dt, "cuda", transform=True)
+
+        def rstep():
+            vts.topk_transform_ragged(x, L, off, k, row_starts=rs, out=o, workspace=ws)
+        return rstep, ws
     pt = torch.from_numpy(wl.page_table).cuda()
     pr = torch.from_numpy(wl.page_table_row_starts).cuda()
     out = torch.empty((R, k), dtype=torch.int32, device="cuda")
@@ -363,18 +371,18 @@ def main() -> int:
 
     if not args.no_others:
         others = {}
-        for name in ("small", "dsv32", "long", "dsv4_mtp", "page"):
+        for name in ("small", "dsv32", "long", "dsv4_mtp", "page", "page_ragged"):
             if name == args.workload:
                 continue
             log(f"workload {name}")
-            w2 = workloads.make(name)
+            w2 = workloads.make(name.replace("_ragged", ""))
             n2 = valid_lengths(w2)
-            s2, ws2 = make_step(w2, torch, vts)
+            s2, ws2 = make_step(w2, torch, vts, ragged=name.endswith("_ragged"))
             for _ in range(5):
                 s2()
             ct2 = cold_times(s2, torch, 20)
             vb2 = int(n2.sum()) * (4 if w2.dtype == 0 else 2)
-            others[w2.name] = {
+            others[name] = {
                 "us_median_cold": round(float(np.median(ct2)), 2),
                 "valid_GBps": round(vb2 / (np.median(ct2) * 1e-6) / 1e9, 1),
                 "valid_bytes": vb2}

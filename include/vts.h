@@ -155,6 +155,30 @@ int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num
                                   int32_t top_k, int32_t* out, int32_t* out_raw_indices,
                                   void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * vts_topk_transform_ragged -- top-k over row windows with the ragged-KV index
+ * transform (SGLang TopK_Ops page, fast_topk_transform_ragged_fused: the
+ * offset of each row's top-k indices in a ragged KV buffer).
+ *
+ * scores, lengths, row_starts, top_k, workspace: as for
+ *              vts_topk_page_table_transform (workspace sized by
+ *              vts_page_transform_workspace_bytes).
+ * topk_indices_offset device int32[num_rows]: added to every selected
+ *              window-relative index of the row (int32 arithmetic; keeping
+ *              the sums in range is the caller's contract).
+ * out          device int32[num_rows, top_k], 16-byte aligned: idx +
+ *              topk_indices_offset[r] for each selected window-relative
+ *              index idx, -1 in unused slots.
+ * out_raw_indices device int32[num_rows, top_k] or NULL: the window-relative
+ *              indices, positionally aligned with `out`, -1 in unused slots.
+ *              Must not overlap `out`.
+ */
+int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                              int64_t row_stride, const int32_t* lengths,
+                              const int32_t* row_starts, const int32_t* topk_indices_offset,
+                              int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Aliases with the operation names of the pages. */
 int topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
                 int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,

@@ -158,6 +158,26 @@ def page_translate(raw: np.ndarray, page_table: np.ndarray, page_table_row_start
     return out
 
 
+def ragged_translate(raw: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """Ragged-KV transform of window-relative indices (SGLang TopK_Ops page,
+    fast_topk_transform_ragged_fused): idx + topk_indices_offset[r], -1 kept."""
+    raw = np.asarray(raw, dtype=np.int64)
+    off = np.asarray(offsets, dtype=np.int64).reshape(-1, 1)
+    out = np.where(raw < 0, -1, raw + off)
+    if np.any(out > np.iinfo(np.int32).max) or np.any((raw >= 0) & (out < np.iinfo(np.int32).min)):
+        raise OverflowError("translated index does not fit in int32")
+    return out.astype(np.int32)
+
+
+def topk_transform_ragged(scores: np.ndarray, dtype: int, lengths: np.ndarray, row_starts,
+                          offsets: np.ndarray, k: int, nthreads: int | None = None):
+    """Oracle of the ragged transform: (out, out_raw, base, n)."""
+    R, W = scores.shape
+    base, n = window_rows(lengths, row_starts, W)
+    raw, _ = select(scores, dtype, base, n, k, False, nthreads)
+    return ragged_translate(raw, offsets), raw, base, n
+
+
 def topk_varlen(logits: np.ndarray, dtype: int, seq_lens: np.ndarray, k: int, next_n: int = 1,
                 compress_ratio: int = 1, return_values: bool = False, nthreads: int | None = None):
     """Oracle of topk_varlen: (idx, values-or-None, n per row)."""

@@ -286,6 +286,43 @@ def test_transform_out_of_table_page_is_minus_one():
     assert out[0].tolist() == [5 * 64, 5 * 64 + 63, 7 * 64, -1]
 
 
+def test_ragged_transform_hand_worked():
+    # row 0: the three largest of [1, 5, 3, 9, 7] are columns 3, 4, 1 (9, 7, 5);
+    # row 1: window of 2 columns <= k, so the identity then -1 (short-row rule)
+    x = np.array([[1, 5, 3, 9, 7], [4, 2, 8, 6, 0]], np.float32)
+    L = np.array([5, 2], np.int32)
+    off = np.array([100, 7], np.int32)
+    out, raw, base, n = oracle.topk_transform_ragged(x, F32, L, None, off, 3)
+    assert raw.tolist() == [[3, 4, 1], [0, 1, -1]]
+    assert out.tolist() == [[103, 104, 101], [7, 8, -1]]
+
+
+def test_ragged_transform_identities():
+    rng = np.random.default_rng(12)
+    R, W, k = 7, 3000, 64
+    x = rng.standard_normal((R, W)).astype(np.float32)
+    L = rng.integers(0, 1500, size=R).astype(np.int32)
+    rs = rng.integers(0, W - 1500, size=R).astype(np.int32)
+    zero = np.zeros(R, np.int32)
+    out0, raw0, _, _ = oracle.topk_transform_ragged(x, F32, L, rs, zero, k)
+    assert np.array_equal(out0, raw0)  # offset 0: the raw indices
+    off = rng.integers(0, 1 << 30, size=R).astype(np.int32)
+    out, raw, base, n = oracle.topk_transform_ragged(x, F32, L, rs, off, k)
+    assert np.array_equal(raw, raw0)  # the selection ignores the offsets
+    sel = raw >= 0
+    assert np.array_equal((out - off[:, None])[sel], raw[sel])
+    assert np.all(out[~sel] == -1)
+    # the selection is the page transform's (same windows): identity table, page 1
+    pt = np.tile(np.arange(W, dtype=np.int32), (R, 1))
+    pout, praw, _, _ = oracle.topk_page_table_transform(x, F32, L, rs, pt, rs, 1, k)
+    assert np.array_equal(praw, raw)
+
+
+def test_ragged_transform_overflow_is_flagged():
+    with pytest.raises(OverflowError):
+        oracle.ragged_translate(np.array([[5]], np.int32), np.array([2 ** 31 - 3], np.int64))
+
+
 # --------------------------------------------------------------------------
 # the checker rejects wrong answers and accepts tie-equivalent ones
 # --------------------------------------------------------------------------

@@ -7,6 +7,7 @@ library is missing or the device is not gfx950, the calls raise.
 
     topk_varlen(logits, seq_lens, top_k, ...)            -> (indices, values | None)
     topk_page_table_transform(scores, lengths, table, top_k, ...) -> (out, out_raw | None)
+    topk_transform_ragged(scores, lengths, offsets, top_k, ...)   -> (out, out_raw | None)
 
 The C entry points, their argument contracts and the page citations are in
 ``include/vts.h``.
@@ -19,7 +20,8 @@ import warnings
 
 import torch
 
-__all__ = ["topk_varlen", "topk_page_table_transform", "workspace_bytes", "make_workspace",
+__all__ = ["topk_varlen", "topk_page_table_transform", "topk_transform_ragged",
+           "workspace_bytes", "make_workspace",
            "set_tuning", "workspace_stats", "VtsError", "library", "LIB_PATH"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +56,9 @@ def library():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.vts_topk_varlen.restype = ctypes.c_int
     lib.vts_topk_varlen.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.vts_topk_transform_ragged.restype = ctypes.c_int
+    lib.vts_topk_transform_ragged.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp, vp, vp,
+                                              sz, vp]
     lib.vts_topk_page_table_transform.restype = ctypes.c_int
     lib.vts_topk_page_table_transform.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i64, i64, vp,
                                                   i32, i32, vp, vp, vp, sz, vp]
@@ -214,6 +219,34 @@ def topk_page_table_transform(scores: torch.Tensor, lengths: torch.Tensor,
         _ptr(page_table_row_starts), page_size, top_k, o.data_ptr(), _ptr(raw),
         workspace.data_ptr(), workspace.numel(), sp)
     _check("vts_topk_page_table_transform", st)
+    return o, raw
+
+
+def topk_transform_ragged(scores: torch.Tensor, lengths: torch.Tensor,
+                          topk_indices_offset: torch.Tensor, top_k: int,
+                          row_starts: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                          out_raw_indices: torch.Tensor | None = None, return_raw: bool = False,
+                          workspace: torch.Tensor | None = None, stream=None):
+    """Top-k over row windows, each index offset into a ragged KV buffer (include/vts.h)."""
+    _check_scores(scores, "scores")
+    R, W = scores.shape
+    dev = scores.device
+    lengths = _i32(lengths, "lengths", R, dev)
+    offsets = _i32(topk_indices_offset, "topk_indices_offset", R, dev)
+    if row_starts is not None:
+        row_starts = _i32(row_starts, "row_starts", R, dev)
+    o = _out(out, (R, top_k), torch.int32, dev, "out")
+    raw = None
+    if out_raw_indices is not None or return_raw:
+        raw = _out(out_raw_indices, (R, top_k), torch.int32, dev, "out_raw_indices")
+    sp = _stream_ptr(stream, dev)
+    if workspace is None:
+        workspace = _default_workspace(workspace_bytes(R, W, top_k, scores.dtype, True), dev, sp)
+    st = library().vts_topk_transform_ragged(
+        scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
+        lengths.data_ptr(), _ptr(row_starts), offsets.data_ptr(), top_k, o.data_ptr(), _ptr(raw),
+        workspace.data_ptr(), workspace.numel(), sp)
+    _check("vts_topk_transform_ragged", st)
     return o, raw
 
 

@@ -259,6 +259,45 @@ int topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_row
                                          out, out_raw_indices, workspace, workspace_bytes_, stream);
 }
 
+int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                              int64_t row_stride, const int32_t* lengths,
+                              const int32_t* row_starts, const int32_t* topk_indices_offset,
+                              int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                              void* workspace, size_t workspace_bytes_, void* stream) {
+    int st = check_rows(scores, dtype, num_rows, width, row_stride, top_k);
+    if (st != VTS_OK) return st;
+    if (num_rows == 0) return VTS_OK;
+    if (lengths == nullptr || topk_indices_offset == nullptr) return VTS_ERR_INVALID;
+    if (out == nullptr || !aligned(out, 16)) return VTS_ERR_INVALID;
+    if (out_raw_indices && !aligned(out_raw_indices, 16)) return VTS_ERR_INVALID;
+    const size_t nk = (size_t)num_rows * (size_t)top_k;
+    if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (st != VTS_OK) return st;
+    st = check_device();
+    if (st != VTS_OK) return st;
+
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.x = scores;
+    p.row_stride = row_stride;
+    p.width = width;
+    p.num_rows = (int32_t)num_rows;
+    p.k = top_k;
+    p.next_n = 1;
+    p.cr = 1;
+    p.lengths = lengths;
+    p.row_starts = row_starts;
+    p.offsets = topk_indices_offset;
+    p.page_size = 1;
+    p.out_idx = out;
+    p.out_raw = out_raw_indices;
+    fill_plan(p, num_rows, width, workspace);
+    if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return VTS_ERR_HIP;
+    return VTS_OK;
+}
+
 const char* vts_status_string(int status) {
     switch (status) {
         case VTS_OK: return "ok";

@@ -42,6 +42,7 @@ struct Params {
     int64_t pt_width;
     const int32_t* ptrs;
     int32_t page_size;
+    const int32_t* offsets;  // ragged transform: per-row index offset (null: page table)
     // outputs
     int32_t* out_idx;  // topk_varlen: indices; transform: translated `out`
     void* out_vals;    // topk_varlen values or null

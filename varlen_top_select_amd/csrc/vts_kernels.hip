@@ -112,6 +112,9 @@ struct PagePolicy {
     // table also gives -1.
     __device__ __forceinline__ static int32_t translate(const Params& p, int r, int64_t base, int32_t col) {
         if (col < 0) return -1;
+        // SGLang TopK_Ops, fast_topk_transform_ragged_fused: the index plus the
+        // row's offset in the ragged KV (int32 arithmetic: caller's contract)
+        if (p.offsets) return (int32_t)((uint32_t)col + (uint32_t)gload(p.offsets + r));
         const int64_t start = p.ptrs ? (int64_t)gload(p.ptrs + r) : base;
         const int64_t pc = start + col / p.page_size;
         if (pc < 0 || pc >= p.pt_width) return -1;
