@@ -85,7 +85,7 @@ def upload(wl, torch):
     return raw.view(dt)[:, : wl.width], dt
 
 
-def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False):
+def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False, page1: bool = False):
     """Returns (step, out tensors, workspace) for one call of the whole batch."""
     x, dt = upload(wl, torch)
     R, k = wl.rows, wl.k
@@ -111,6 +111,16 @@ def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False):
         def rstep():
             vts.topk_transform_ragged(x, L, off, k, row_starts=rs, out=o, workspace=ws)
         return rstep, ws
+    if page1:  # the same windows, one row per request, a page-size-1 table per request
+        g = np.random.default_rng(7)
+        pt1 = torch.from_numpy(g.integers(0, 1 << 30, size=(R, wl.width), dtype=np.int32)).cuda()
+        cu = torch.arange(R + 1, dtype=torch.int32, device="cuda")
+        o = torch.empty((R, k), dtype=torch.int32, device="cuda")
+        ws = vts.make_workspace(R, wl.width, k, dt, "cuda", transform=True)
+
+        def pstep():
+            vts.topk_transform_page1(x, L, pt1, cu, k, row_starts=rs, out=o, workspace=ws)
+        return pstep, ws
     pt = torch.from_numpy(wl.page_table).cuda()
     pr = torch.from_numpy(wl.page_table_row_starts).cuda()
     out = torch.empty((R, k), dtype=torch.int32, device="cuda")
@@ -371,13 +381,14 @@ def main() -> int:
 
     if not args.no_others:
         others = {}
-        for name in ("small", "dsv32", "long", "dsv4_mtp", "page", "page_ragged"):
+        for name in ("small", "dsv32", "long", "dsv4_mtp", "page", "page_ragged", "page_page1"):
             if name == args.workload:
                 continue
             log(f"workload {name}")
-            w2 = workloads.make(name.replace("_ragged", ""))
+            w2 = workloads.make(name.split("_")[0] if name.startswith("page") else name)
             n2 = valid_lengths(w2)
-            s2, ws2 = make_step(w2, torch, vts, ragged=name.endswith("_ragged"))
+            s2, ws2 = make_step(w2, torch, vts, ragged=name.endswith("_ragged"),
+                                page1=name.endswith("_page1"))
             for _ in range(5):
                 s2()
             ct2 = cold_times(s2, torch, 20)

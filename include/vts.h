@@ -179,6 +179,37 @@ int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_row
                               int32_t top_k, int32_t* out, int32_t* out_raw_indices,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * vts_topk_transform_page1 -- top-k over row windows with the page-size-1
+ * transform of SGLang's fast_topk_transform_fused (TopK_Ops page): each row
+ * is a query of one request, found through `cu_seqlens_q`, and each selected
+ * window-relative index (a KV position of that request) is replaced by the
+ * request's page-table entry for it.
+ *
+ * scores, lengths, row_starts, top_k: as for vts_topk_page_table_transform.
+ * page_table   device int32, num_batches rows of page_table_width entries,
+ *              page_table_stride entries apart: row b maps KV positions of
+ *              request b to physical KV slots.
+ * cu_seqlens_q device int32[num_batches + 1], non-decreasing: rows
+ *              [cu_seqlens_q[b], cu_seqlens_q[b + 1]) belong to request b.
+ * out          device int32[num_rows, top_k], 16-byte aligned:
+ *              page_table[b(r), idx] for each selected index idx, -1 in
+ *              unused slots, where idx >= page_table_width, and in every slot
+ *              of a row outside [cu_seqlens_q[0], cu_seqlens_q[num_batches]).
+ * out_raw_indices device int32[num_rows, top_k] or NULL: the window-relative
+ *              indices, positionally aligned with `out`; must not overlap it.
+ * workspace    as for vts_topk_varlen, sized by vts_page_transform_workspace_bytes;
+ *              the call also writes a row-to-request map into it (a small
+ *              kernel on `stream` before the selection).
+ */
+int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                             int64_t row_stride, const int32_t* lengths, const int32_t* row_starts,
+                             const int32_t* page_table, int64_t page_table_stride,
+                             int64_t page_table_width, const int32_t* cu_seqlens_q,
+                             int64_t num_batches, int32_t top_k, int32_t* out,
+                             int32_t* out_raw_indices, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* Aliases with the operation names of the pages. */
 int topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
                 int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,

@@ -169,6 +169,45 @@ def ragged_translate(raw: np.ndarray, offsets: np.ndarray) -> np.ndarray:
     return out.astype(np.int32)
 
 
+def row_requests(cu_seqlens_q: np.ndarray, num_rows: int) -> np.ndarray:
+    """Request of each row (SGLang TopK_Ops page, `cu_seqlens_q`): the b with
+    cu[b] <= r < cu[b + 1], or -1 outside [cu[0], cu[-1])."""
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    r = np.arange(num_rows, dtype=np.int64)
+    b = np.searchsorted(cu, r, side="right") - 1
+    inside = (r >= cu[0]) & (r < cu[-1]) if cu.size > 1 else np.zeros(num_rows, bool)
+    return np.where(inside, b, -1)
+
+
+def page1_translate(raw: np.ndarray, page_table: np.ndarray, cu_seqlens_q: np.ndarray) -> np.ndarray:
+    """Page-size-1 transform (SGLang TopK_Ops page, fast_topk_transform_fused):
+    page_table[b(r), idx], -1 for unused slots, rows outside every request and
+    indices past the table."""
+    raw = np.asarray(raw, dtype=np.int64)
+    R, k = raw.shape
+    pt = np.asarray(page_table, dtype=np.int64)
+    b = row_requests(cu_seqlens_q, R)
+    out = np.full((R, k), -1, np.int64)
+    for r in range(R):
+        if b[r] < 0:
+            continue
+        for j in range(k):
+            i = raw[r, j]
+            if 0 <= i < pt.shape[1]:
+                out[r, j] = pt[b[r], i]
+    return out.astype(np.int32)
+
+
+def topk_transform_page1(scores: np.ndarray, dtype: int, lengths: np.ndarray, row_starts,
+                         page_table: np.ndarray, cu_seqlens_q: np.ndarray, k: int,
+                         nthreads: int | None = None):
+    """Oracle of the page-size-1 transform: (out, out_raw, base, n)."""
+    R, W = scores.shape
+    base, n = window_rows(lengths, row_starts, W)
+    raw, _ = select(scores, dtype, base, n, k, False, nthreads)
+    return page1_translate(raw, page_table, cu_seqlens_q), raw, base, n
+
+
 def topk_transform_ragged(scores: np.ndarray, dtype: int, lengths: np.ndarray, row_starts,
                           offsets: np.ndarray, k: int, nthreads: int | None = None):
     """Oracle of the ragged transform: (out, out_raw, base, n)."""

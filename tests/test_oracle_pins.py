@@ -318,6 +318,52 @@ def test_ragged_transform_identities():
     assert np.array_equal(praw, raw)
 
 
+def test_row_requests_brute_force():
+    # cu = [2, 2, 5, 6]: rows 0-1 and 6+ are outside, request 0 is empty,
+    # rows 2-4 belong to request 1, row 5 to request 2
+    cu = np.array([2, 2, 5, 6], np.int32)
+    assert oracle.row_requests(cu, 8).tolist() == [-1, -1, 1, 1, 1, 2, -1, -1]
+    rng = np.random.default_rng(13)
+    cu = np.concatenate([[0], np.cumsum(rng.integers(0, 4, size=50))]).astype(np.int32)
+    R = int(cu[-1]) + 3
+    got = oracle.row_requests(cu, R)
+    for r in range(R):
+        want = [b for b in range(len(cu) - 1) if cu[b] <= r < cu[b + 1]]
+        assert got[r] == (want[0] if want else -1)
+
+
+def test_page1_transform_hand_worked():
+    # two requests: rows 0-1 -> request 0, row 2 -> request 1
+    x = np.array([[1, 5, 3, 9, 7], [4, 2, 8, 6, 0], [0, 1, 2, 3, 4]], np.float32)
+    L = np.array([5, 5, 2], np.int32)
+    pt = np.array([[10, 11, 12, 13, 14], [20, 21, 22, 23, 24]], np.int32)
+    cu = np.array([0, 2, 3], np.int32)
+    out, raw, base, n = oracle.topk_transform_page1(x, F32, L, None, pt, cu, 3)
+    assert raw.tolist() == [[3, 4, 1], [2, 3, 0], [0, 1, -1]]
+    assert out.tolist() == [[13, 14, 11], [12, 13, 10], [20, 21, -1]]
+
+
+def test_page1_transform_identity_and_permutation():
+    rng = np.random.default_rng(14)
+    B, W, k = 6, 2000, 40
+    cu = np.concatenate([[0], np.cumsum(rng.integers(1, 4, size=B))]).astype(np.int32)
+    R = int(cu[-1])
+    x = rng.standard_normal((R, W)).astype(np.float32)
+    L = rng.integers(0, W, size=R).astype(np.int32)
+    ident = np.tile(np.arange(W, dtype=np.int32), (B, 1))
+    out, raw, _, _ = oracle.topk_transform_page1(x, F32, L, None, ident, cu, k)
+    assert np.array_equal(out, raw)  # identity table: the raw indices
+    perm = np.stack([rng.permutation(W) for _ in range(B)]).astype(np.int32)
+    out, raw2, _, _ = oracle.topk_transform_page1(x, F32, L, None, perm, cu, k)
+    assert np.array_equal(raw2, raw)
+    b = oracle.row_requests(cu, R)
+    inv = np.argsort(perm, axis=1)
+    sel = raw >= 0
+    rows = np.nonzero(sel)[0]
+    assert np.array_equal(inv[b[rows], out[sel]], raw[sel])  # the table is undone per request
+    assert np.all(out[~sel] == -1)
+
+
 def test_ragged_transform_overflow_is_flagged():
     with pytest.raises(OverflowError):
         oracle.ragged_translate(np.array([[5]], np.int32), np.array([2 ** 31 - 3], np.int64))

@@ -8,6 +8,7 @@ library is missing or the device is not gfx950, the calls raise.
     topk_varlen(logits, seq_lens, top_k, ...)            -> (indices, values | None)
     topk_page_table_transform(scores, lengths, table, top_k, ...) -> (out, out_raw | None)
     topk_transform_ragged(scores, lengths, offsets, top_k, ...)   -> (out, out_raw | None)
+    topk_transform_page1(scores, lengths, table, cu_seqlens_q, top_k, ...) -> (out, out_raw | None)
 
 The C entry points, their argument contracts and the page citations are in
 ``include/vts.h``.
@@ -21,6 +22,7 @@ import warnings
 import torch
 
 __all__ = ["topk_varlen", "topk_page_table_transform", "topk_transform_ragged",
+           "topk_transform_page1",
            "workspace_bytes", "make_workspace",
            "set_tuning", "workspace_stats", "VtsError", "library", "LIB_PATH"]
 
@@ -56,6 +58,9 @@ def library():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.vts_topk_varlen.restype = ctypes.c_int
     lib.vts_topk_varlen.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.vts_topk_transform_page1.restype = ctypes.c_int
+    lib.vts_topk_transform_page1.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i64, i64, vp, i64,
+                                             i32, vp, vp, vp, sz, vp]
     lib.vts_topk_transform_ragged.restype = ctypes.c_int
     lib.vts_topk_transform_ragged.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp, vp, vp,
                                               sz, vp]
@@ -247,6 +252,40 @@ def topk_transform_ragged(scores: torch.Tensor, lengths: torch.Tensor,
         lengths.data_ptr(), _ptr(row_starts), offsets.data_ptr(), top_k, o.data_ptr(), _ptr(raw),
         workspace.data_ptr(), workspace.numel(), sp)
     _check("vts_topk_transform_ragged", st)
+    return o, raw
+
+
+def topk_transform_page1(scores: torch.Tensor, lengths: torch.Tensor, page_table: torch.Tensor,
+                         cu_seqlens_q: torch.Tensor, top_k: int,
+                         row_starts: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                         out_raw_indices: torch.Tensor | None = None, return_raw: bool = False,
+                         workspace: torch.Tensor | None = None, stream=None):
+    """Top-k over row windows with the page-size-1, per-request page-table
+    transform (include/vts.h, vts_topk_transform_page1)."""
+    _check_scores(scores, "scores")
+    R, W = scores.shape
+    dev = scores.device
+    lengths = _i32(lengths, "lengths", R, dev)
+    if row_starts is not None:
+        row_starts = _i32(row_starts, "row_starts", R, dev)
+    pt = page_table
+    if pt.dtype != torch.int32 or pt.dim() != 2 or pt.device != dev or pt.stride(1) != 1:
+        raise ValueError("page_table must be a 2-D int32 tensor with contiguous rows")
+    B = pt.shape[0]
+    cu = _i32(cu_seqlens_q, "cu_seqlens_q", B + 1, dev)
+    o = _out(out, (R, top_k), torch.int32, dev, "out")
+    raw = None
+    if out_raw_indices is not None or return_raw:
+        raw = _out(out_raw_indices, (R, top_k), torch.int32, dev, "out_raw_indices")
+    sp = _stream_ptr(stream, dev)
+    if workspace is None:
+        workspace = _default_workspace(workspace_bytes(R, W, top_k, scores.dtype, True), dev, sp)
+    st = library().vts_topk_transform_page1(
+        scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
+        lengths.data_ptr(), _ptr(row_starts), pt.data_ptr(), pt.stride(0), pt.shape[1],
+        cu.data_ptr(), B, top_k, o.data_ptr(), _ptr(raw), workspace.data_ptr(), workspace.numel(),
+        sp)
+    _check("vts_topk_transform_page1", st)
     return o, raw
 
 

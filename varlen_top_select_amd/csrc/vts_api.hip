@@ -298,6 +298,58 @@ int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_row
     return VTS_OK;
 }
 
+int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                             int64_t row_stride, const int32_t* lengths, const int32_t* row_starts,
+                             const int32_t* page_table, int64_t page_table_stride,
+                             int64_t page_table_width, const int32_t* cu_seqlens_q,
+                             int64_t num_batches, int32_t top_k, int32_t* out,
+                             int32_t* out_raw_indices, void* workspace, size_t workspace_bytes_,
+                             void* stream) {
+    int st = check_rows(scores, dtype, num_rows, width, row_stride, top_k);
+    if (st != VTS_OK) return st;
+    if (num_batches < 0 || num_batches > INT32_MAX - 1) return VTS_ERR_INVALID;
+    if (page_table_width < 1 || page_table_stride < page_table_width) return VTS_ERR_INVALID;
+    if (num_rows == 0) return VTS_OK;
+    if (lengths == nullptr || page_table == nullptr || cu_seqlens_q == nullptr)
+        return VTS_ERR_INVALID;
+    if (out == nullptr || !aligned(out, 16)) return VTS_ERR_INVALID;
+    if (out_raw_indices && !aligned(out_raw_indices, 16)) return VTS_ERR_INVALID;
+    const size_t nk = (size_t)num_rows * (size_t)top_k;
+    if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (st != VTS_OK) return st;
+    st = check_device();
+    if (st != VTS_OK) return st;
+
+    Params p;
+    memset(&p, 0, sizeof(p));
+    p.x = scores;
+    p.row_stride = row_stride;
+    p.width = width;
+    p.num_rows = (int32_t)num_rows;
+    p.k = top_k;
+    p.next_n = 1;
+    p.cr = 1;
+    p.lengths = lengths;
+    p.row_starts = row_starts;
+    p.pt = page_table;
+    p.pt_stride = page_table_stride;
+    p.pt_width = page_table_width;
+    p.page_size = 1;
+    p.out_idx = out;
+    p.out_raw = out_raw_indices;
+    fill_plan(p, num_rows, width, workspace);
+    const WsLayout L = ws_layout(num_rows, p.nsplit);
+    int32_t* row_batch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.batch);
+    p.row_batch = row_batch;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (launch_row_batch(cu_seqlens_q, (int32_t)num_batches, (int32_t)num_rows, row_batch, s) !=
+        hipSuccess)
+        return VTS_ERR_HIP;
+    if (launch_transform(dtype, p, s) != hipSuccess) return VTS_ERR_HIP;
+    return VTS_OK;
+}
+
 const char* vts_status_string(int status) {
     switch (status) {
         case VTS_OK: return "ok";

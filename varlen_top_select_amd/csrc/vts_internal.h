@@ -43,6 +43,7 @@ struct Params {
     const int32_t* ptrs;
     int32_t page_size;
     const int32_t* offsets;  // ragged transform: per-row index offset (null: page table)
+    const int32_t* row_batch;  // page-size-1 transform: each row's request (page-table row), or -1
     // outputs
     int32_t* out_idx;  // topk_varlen: indices; transform: translated `out`
     void* out_vals;    // topk_varlen values or null
@@ -71,7 +72,7 @@ enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };
 
 // Workspace layout (bytes from the base): stats, tickets, counts, keys, indices.
 struct WsLayout {
-    size_t stats, ticket, count, count_up, key, idx, total;
+    size_t stats, ticket, count, count_up, key, idx, batch, total;
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -85,11 +86,15 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
     L.count_up = L.count + align256(units * 4);
     L.key = L.count_up + align256(units * 4);
     L.idx = L.key + align256(units * WSCAP * 4);
-    L.total = L.idx + align256(units * WSCAP * 4);
+    L.batch = L.idx + align256(units * WSCAP * 4);  // one int32 per row (request map)
+    L.total = L.batch + align256((size_t)num_rows * 4);
     return L;
 }
 
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream);
+// Writes each row's request b (cu_seqlens[b] <= row < cu_seqlens[b + 1]) or -1.
+hipError_t launch_row_batch(const int32_t* cu_seqlens, int32_t num_batches, int32_t num_rows,
+                            int32_t* row_batch, hipStream_t stream);
 
 }  // namespace vts

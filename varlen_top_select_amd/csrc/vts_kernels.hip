@@ -115,6 +115,13 @@ struct PagePolicy {
         // SGLang TopK_Ops, fast_topk_transform_ragged_fused: the index plus the
         // row's offset in the ragged KV (int32 arithmetic: caller's contract)
         if (p.offsets) return (int32_t)((uint32_t)col + (uint32_t)gload(p.offsets + r));
+        // SGLang TopK_Ops, fast_topk_transform_fused: page size 1, the table
+        // row of the row's request, the index itself as the table column
+        if (p.row_batch) {
+            const int32_t b = gload(p.row_batch + r);
+            if (b < 0 || (int64_t)col >= p.pt_width) return -1;
+            return gload(p.pt + (int64_t)b * p.pt_stride + col);
+        }
         const int64_t start = p.ptrs ? (int64_t)gload(p.ptrs + r) : base;
         const int64_t pc = start + col / p.page_size;
         if (pc < 0 || pc >= p.pt_width) return -1;
@@ -1393,6 +1400,34 @@ hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream) {
         case F16: return launch_dt<F16, VarlenPolicy>(p, stream);
     }
     return hipErrorInvalidValue;
+}
+
+// Row -> request map of the page-size-1 transform: row r belongs to the request
+// b with cu_seqlens[b] <= r < cu_seqlens[b + 1] (SGLang TopK_Ops,
+// `cu_seqlens_q`), found by binary search over the non-decreasing offsets; a
+// row outside [cu_seqlens[0], cu_seqlens[num_batches]) gets -1.
+__global__ void __launch_bounds__(NT) row_batch_kernel(const int32_t* cu, int32_t nb, int32_t rows,
+                                                       int32_t* row_batch) {
+    const int32_t r = (int32_t)(blockIdx.x * NT + threadIdx.x);
+    if (r >= rows) return;
+    int32_t b = -1;
+    if (nb > 0 && gload(cu) <= r && r < gload(cu + nb)) {
+        int32_t lo = 0, hi = nb;  // cu[lo] <= r < cu[hi]
+        while (hi - lo > 1) {
+            const int32_t mid = lo + (hi - lo) / 2;
+            if (gload(cu + mid) <= r) lo = mid; else hi = mid;
+        }
+        b = lo;
+    }
+    gstore(row_batch + r, b);
+}
+
+hipError_t launch_row_batch(const int32_t* cu_seqlens, int32_t num_batches, int32_t num_rows,
+                            int32_t* row_batch, hipStream_t stream) {
+    const uint32_t grid = ((uint32_t)num_rows + NT - 1) / NT;
+    hipLaunchKernelGGL(row_batch_kernel, dim3(grid), dim3(NT), 0, stream, cu_seqlens, num_batches,
+                       num_rows, row_batch);
+    return hipGetLastError();
 }
 
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream) {
