@@ -2,9 +2,10 @@
 //
 //  * order-preserving unsigned keys for fp32 / bf16 / fp16;
 //  * wave64 ballot / mbcnt helpers and wave-aggregated LDS counters;
-//  * a workgroup radix select (8-bit digits, LDS histogram, scan over the
-//    256 bins) that finds the exact r-th largest key of any key set that the
-//    workgroup can enumerate.
+//  * a workgroup radix select (10-bit digits from the first bit in which the
+//    keys differ, a padded 1024-bin LDS histogram scanned by one wave) that
+//    finds the exact r-th largest key of any key set that the workgroup can
+//    enumerate, and a paired variant that finds two ranks at once.
 #pragma once
 
 #include <hip/hip_runtime.h>

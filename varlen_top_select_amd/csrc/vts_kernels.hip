@@ -599,7 +599,7 @@ __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col
 }
 
 // One streaming step with both rungs >= +0.  Per vector: the largest raw
-// element against the lower rung; the (few) vectors holding a candidate are
+// element against the safe rung T; the (few) vectors holding a candidate are
 // appended to the wave's staging queue in LDS (ballot + mbcnt positions).
 // Whenever STAGE_DRAIN are queued, a round of STAGE_DRAIN is drained and the
 // rest moves to the front, so the per-element work runs on rounds of staged
