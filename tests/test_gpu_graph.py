@@ -12,8 +12,10 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import varlen_top_select_amd as vts
 import workloads
+from oracle.check import check_rows
 from tests.gpu_util import (RAW_TORCH, TORCH_DTYPE, check_transform_wl, check_varlen, say)
 
 pytestmark = pytest.mark.gpu
@@ -121,3 +123,64 @@ def test_graph_replay_page_transform():
         torch.cuda.synchronize()
         errs = check_transform_wl(wl, out.cpu().numpy(), rawi.cpu().numpy())
         assert errs == [], f"replay {rep}: " + "\n".join(errs)
+
+
+@pytest.mark.parametrize("variant", ["ragged", "page1"])
+def test_graph_replay_sglang_transforms(variant):
+    """The ragged-KV and the page-size-1 transforms (the latter is two launches:
+    the row-to-request map, then the selection) replayed on changing inputs."""
+    from tests.test_gpu_transforms import _requests
+    wls = [workloads.make("page", seed=s, rows=24) for s in SEEDS]
+    w0 = wls[0]
+    R, k, dt = w0.rows, w0.k, TORCH_DTYPE[w0.dtype]
+    rng = np.random.default_rng(90)
+    raw = _raw(w0).cuda()
+    x = raw.view(dt)[:, : w0.width]
+    L = torch.from_numpy(w0.lengths).cuda()
+    rs = torch.from_numpy(w0.row_starts).cuda()
+    off = torch.zeros(R, dtype=torch.int32, device="cuda")
+    cu_np = _requests(rng, R)
+    B = len(cu_np) - 1
+    cu = torch.from_numpy(cu_np).cuda()
+    pt = torch.zeros((B, w0.width), dtype=torch.int32, device="cuda")
+    out = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    rawi = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    ws = vts.make_workspace(R, w0.width, k, dt, "cuda", transform=True)
+    torch.cuda.synchronize()
+
+    def call():
+        if variant == "ragged":
+            vts.topk_transform_ragged(x, L, off, k, row_starts=rs, out=out, out_raw_indices=rawi,
+                                      workspace=ws)
+        else:
+            vts.topk_transform_page1(x, L, pt, cu, k, row_starts=rs, out=out,
+                                     out_raw_indices=rawi, workspace=ws)
+
+    say(f"graph capture {variant}")
+    g = _capture(call)
+    for rep, wl in enumerate(wls + wls[:1]):
+        raw.copy_(_raw(wl))
+        L.copy_(torch.from_numpy(wl.lengths))
+        rs.copy_(torch.from_numpy(wl.row_starts))
+        off_np = rng.integers(0, 1 << 28, size=R).astype(np.int32)
+        pt_np = rng.integers(0, 1 << 30, size=(B, wl.width)).astype(np.int32)
+        off.copy_(torch.from_numpy(off_np))
+        pt.copy_(torch.from_numpy(pt_np))
+        out.fill_(-7)
+        rawi.fill_(-7)
+        torch.cuda.synchronize()
+        say(f"graph replay {rep} {variant}")
+        g.replay()
+        torch.cuda.synchronize()
+        o, r = out.cpu().numpy(), rawi.cpu().numpy()
+        if variant == "ragged":
+            ref_out, ref_raw, base, n = oracle.topk_transform_ragged(
+                wl.x[:, :wl.width], wl.dtype, wl.lengths, wl.row_starts, off_np, k)
+            want = oracle.ragged_translate(r, off_np)
+        else:
+            ref_out, ref_raw, base, n = oracle.topk_transform_page1(
+                wl.x[:, :wl.width], wl.dtype, wl.lengths, wl.row_starts, pt_np, cu_np, k)
+            want = oracle.page1_translate(r, pt_np, cu_np)
+        errs = check_rows(wl.x, wl.dtype, base, n, k, r, ref_raw)
+        assert errs == [], f"replay {rep}: " + "\n".join(errs)
+        assert np.array_equal(o, want), f"replay {rep}: out is not the translation of the raw indices"
