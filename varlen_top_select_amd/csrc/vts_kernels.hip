@@ -49,6 +49,8 @@ namespace vts {
 // ---------------------------------------------------------------------------
 
 struct VarlenPolicy {
+    // the output needs no memory reads of its own
+    static constexpr bool GATHERS = false;
     // FlashInfer top_k_varlen doc, `seq_lens`: row t of request i ranks its
     // first max(0, (seq_lens[i] - next_n + t + 1) // compress_ratio) columns,
     // clamped to the width.
@@ -83,6 +85,8 @@ struct VarlenPolicy {
 };
 
 struct PagePolicy {
+    // each output index is read from a table (or an offset) in memory
+    static constexpr bool GATHERS = true;
     // Window [row_start, row_start + n), n = clamp(length, 0, width - row_start);
     // a start outside [0, width] is an empty row.
     struct Raw {
@@ -110,30 +114,47 @@ struct PagePolicy {
     // FlashInfer page-size PR body: out = table[b, start + idx / page_size] *
     // page_size + idx % page_size; -1 stays -1; a table column outside the
     // table also gives -1.
-    __device__ __forceinline__ static int32_t translate(const Params& p, int r, int64_t base, int32_t col) {
+    // The row's own translation inputs, read once per row: a store between
+    // two reads of them would make the second wait for it.
+    struct Row {
+        int64_t start;  // table column of the window's first page
+        int32_t add;    // ragged offset
+        int32_t b;      // request of the row (page size 1)
+    };
+    __device__ __forceinline__ static Row row(const Params& p, int r, int64_t base) {
+        Row w{base, 0, -1};
+        if (p.offsets)
+            w.add = gload(p.offsets + r);
+        else if (p.row_batch)
+            w.b = gload(p.row_batch + r);
+        else if (p.ptrs)
+            w.start = gload(p.ptrs + r);
+        return w;
+    }
+    // whether translate reads memory (the ragged offset is arithmetic only)
+    __device__ __forceinline__ static bool gathers(const Params& p) { return p.offsets == nullptr; }
+    __device__ __forceinline__ static int32_t translate(const Params& p, int r, const Row& w, int32_t col) {
         if (col < 0) return -1;
         // SGLang TopK_Ops, fast_topk_transform_ragged_fused: the index plus the
         // row's offset in the ragged KV (int32 arithmetic: caller's contract)
-        if (p.offsets) return (int32_t)((uint32_t)col + (uint32_t)gload(p.offsets + r));
+        if (p.offsets) return (int32_t)((uint32_t)col + (uint32_t)w.add);
         // SGLang TopK_Ops, fast_topk_transform_fused: page size 1, the table
         // row of the row's request, the index itself as the table column
         if (p.row_batch) {
-            const int32_t b = gload(p.row_batch + r);
-            if (b < 0 || (int64_t)col >= p.pt_width) return -1;
-            return gload(p.pt + (int64_t)b * p.pt_stride + col);
+            if (w.b < 0 || (int64_t)col >= p.pt_width) return -1;
+            return gload(p.pt + (int64_t)w.b * p.pt_stride + col);
         }
-        const int64_t start = p.ptrs ? (int64_t)gload(p.ptrs + r) : base;
-        const int64_t pc = start + col / p.page_size;
+        const int64_t pc = w.start + col / p.page_size;
         if (pc < 0 || pc >= p.pt_width) return -1;
         const int64_t page = gload(p.pt + (int64_t)r * p.pt_stride + pc);
         return (int32_t)(page * p.page_size + col % p.page_size);
     }
-    template <int DT>
-    __device__ __forceinline__ static void emit(const Params& p, int r, int64_t base, uint32_t pos, int32_t col,
-                                uint32_t) {
-        const int64_t o = (int64_t)r * p.k + pos;
-        gstore(p.out_idx + o, translate(p, r, base, col));
-        if (p.out_raw) gstore(p.out_raw + o, col);
+    // output slot pos: the raw index col, and the translated index t
+    __device__ __forceinline__ static void put_raw(const Params& p, int r, uint32_t pos, int32_t col) {
+        if (p.out_raw) gstore(p.out_raw + (int64_t)r * p.k + pos, col);
+    }
+    __device__ __forceinline__ static void put_idx(const Params& p, int r, uint32_t pos, int32_t t) {
+        gstore(p.out_idx + (int64_t)r * p.k + pos, t);
     }
 };
 
@@ -931,11 +952,19 @@ struct LdsSrc {
             }
         }
     }
+    static constexpr int SLOTS = J;
     template <class F>
     __device__ __forceinline__ void for_each(Smem&, F f) const {
 #pragma unroll
         for (int j = 0; j < J; ++j)
             f((uint32_t)j * NT + threadIdx.x < n && key[j] >= thr, key[j], idx[j]);
+    }
+    // the same, with the register index j as the first argument
+    template <class F>
+    __device__ __forceinline__ void for_each_slot(F f) const {
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            f(j, (uint32_t)j * NT + threadIdx.x < n && key[j] >= thr, key[j], idx[j]);
     }
 };
 
@@ -968,23 +997,93 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
     });
     uint32_t og = wave_ticket_n(&sm.cnt_a, ngt);
     uint32_t oe = wave_ticket_n(&sm.cnt_b, neq);
-    src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
-        const bool isgt = ok && key > K, iseq = ok && key == K;
-        const uint32_t pos = isgt ? og : gt + oe;
-        if (isgt || (iseq && oe < need_eq))
-            Policy::template emit<DT>(p, r, base, pos, (int32_t)col, from_key<DT>(key));
-        og += isgt ? 1u : 0u;
-        oe += iseq ? 1u : 0u;
-    });
+    if constexpr (Policy::GATHERS) {
+        const auto w = Policy::row(p, r, base);
+        if (Policy::gathers(p)) {
+            // Every table read of the thread is issued before its first output
+            // index store.  Placed after a store, a read would wait for it (the
+            // compiler cannot rule out that they overlap, and loads and stores
+            // share one completion counter), one memory round trip per register.
+            // The first pass also writes the raw indices, so the registers that
+            // held them take the translated ones and the pass adds none.
+            const uint32_t og0 = og, oe0 = oe;
+            int32_t tv[Src::SLOTS];
+            src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t col) {
+                const bool isgt = ok && key > K, iseq = ok && key == K;
+                const uint32_t pos = isgt ? og : gt + oe;
+                tv[j] = -1;
+                if (isgt || (iseq && oe < need_eq)) {
+                    Policy::put_raw(p, r, pos, (int32_t)col);
+                    tv[j] = Policy::translate(p, r, w, (int32_t)col);
+                }
+                og += isgt ? 1u : 0u;
+                oe += iseq ? 1u : 0u;
+            });
+            og = og0;
+            oe = oe0;
+            src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t) {
+                const bool isgt = ok && key > K, iseq = ok && key == K;
+                const uint32_t pos = isgt ? og : gt + oe;
+                if (isgt || (iseq && oe < need_eq)) Policy::put_idx(p, r, pos, tv[j]);
+                og += isgt ? 1u : 0u;
+                oe += iseq ? 1u : 0u;
+            });
+        } else {
+            src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+                const bool isgt = ok && key > K, iseq = ok && key == K;
+                const uint32_t pos = isgt ? og : gt + oe;
+                if (isgt || (iseq && oe < need_eq)) {
+                    Policy::put_raw(p, r, pos, (int32_t)col);
+                    Policy::put_idx(p, r, pos, Policy::translate(p, r, w, (int32_t)col));
+                }
+                og += isgt ? 1u : 0u;
+                oe += iseq ? 1u : 0u;
+            });
+        }
+    } else {
+        src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+            const bool isgt = ok && key > K, iseq = ok && key == K;
+            const uint32_t pos = isgt ? og : gt + oe;
+            if (isgt || (iseq && oe < need_eq))
+                Policy::template emit<DT>(p, r, base, pos, (int32_t)col, from_key<DT>(key));
+            og += isgt ? 1u : 0u;
+            oe += iseq ? 1u : 0u;
+        });
+    }
 }
+
+// top_k <= 2048 (the entry points reject more): a short row's outputs fit
+// eight registers per thread
+constexpr int SHORT_J = 8;
+static_assert(SHORT_J * NT >= 2048, "a short row's outputs fit the registers");
 
 template <int DT, class Policy>
 __device__ __forceinline__ void short_row(const Params& p, int r, int64_t base, int64_t n,
                           const typename Traits<DT>::raw_t* row) {
-    for (int j = threadIdx.x; j < p.k; j += NT) {
-        const bool in = j < n;
-        Policy::template emit<DT>(p, r, base, (uint32_t)j, in ? j : -1,
-                                  in ? (uint32_t)gload(row + j) : Traits<DT>::PAD);
+    if constexpr (Policy::GATHERS) {
+        // as in select_and_emit: the table reads before the index stores
+        const auto w = Policy::row(p, r, base);
+        int32_t tv[SHORT_J];
+#pragma unroll
+        for (int u = 0; u < SHORT_J; ++u) {
+            const int j = u * NT + threadIdx.x;
+            tv[u] = -1;
+            if (j < p.k) {
+                Policy::put_raw(p, r, (uint32_t)j, j < n ? j : -1);
+                if (j < n) tv[u] = Policy::translate(p, r, w, j);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < SHORT_J; ++u) {
+            const int j = u * NT + threadIdx.x;
+            if (j < p.k) Policy::put_idx(p, r, (uint32_t)j, tv[u]);
+        }
+    } else {
+        for (int j = threadIdx.x; j < p.k; j += NT) {
+            const bool in = j < n;
+            Policy::template emit<DT>(p, r, base, (uint32_t)j, in ? j : -1,
+                                      in ? (uint32_t)gload(row + j) : Traits<DT>::PAD);
+        }
     }
 }
 
