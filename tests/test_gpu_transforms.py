@@ -110,7 +110,8 @@ def _requests(rng, R, lead=2, tail=1):
     return np.concatenate([[lead], lead + np.cumsum(sizes)]).astype(np.int32)
 
 
-def _run_page1(x_bits, dtype, width, lengths, row_starts, pt, cu, k, tune=None, offset=0):
+def _run_page1(x_bits, dtype, width, lengths, row_starts, pt, cu, k, tune=None, offset=0,
+               with_raw=True):
     R = x_bits.shape[0]
     x = to_device_scores(x_bits, dtype, width, offset)
     L = torch.from_numpy(lengths).cuda()
@@ -124,16 +125,41 @@ def _run_page1(x_bits, dtype, width, lengths, row_starts, pt, cu, k, tune=None, 
         ws = vts.make_workspace(R, width, k, TORCH_DTYPE[dtype], "cuda", transform=True)
         out, raw = vts.topk_transform_page1(x, L, ptd, cud, k, row_starts=rs,
                                             out=ob[pad:pad + R * k],
-                                            out_raw_indices=rb[pad:pad + R * k], workspace=ws)
+                                            out_raw_indices=rb[pad:pad + R * k] if with_raw else None,
+                                            workspace=ws)
         torch.cuda.synchronize()
     o = ob.cpu().numpy()
     assert np.all(o[:pad] == 0x5A5A5A5A) and np.all(o[pad + R * k:] == 0x5A5A5A5A)
-    return out.cpu().numpy(), raw.cpu().numpy()
+    return out.cpu().numpy(), None if raw is None else raw.cpu().numpy()
+
+
+def _unpage1(out, pt, cu):
+    """Raw indices back from page-size-1 outputs, for tables whose rows hold
+    distinct non-negative entries (each a permutation slice): -1 stays -1."""
+    R, k = out.shape
+    raw = np.full((R, k), -1, np.int32)
+    for r in range(R):
+        b = int(np.searchsorted(cu, r, side="right")) - 1
+        if b < 0 or b >= len(cu) - 1:
+            continue
+        order = np.argsort(pt[b], kind="stable")
+        got = out[r] >= 0
+        pos = np.searchsorted(pt[b], out[r][got], sorter=order)
+        assert np.all(pt[b][order[pos]] == out[r][got]), f"row {r}: output not in its table row"
+        raw[r][got] = order[pos]
+    return raw
 
 
 def _check_page1(x_bits, dtype, width, lengths, row_starts, pt, cu, k, out, raw):
     ref_out, ref_raw, base, n = oracle.topk_transform_page1(
         x_bits[:, :width], dtype, lengths, row_starts, pt, cu, k)
+    if raw is None:
+        raw = _unpage1(out, pt, cu)
+        # a row outside every request writes only -1 (checked below): its
+        # selection cannot be read back, so it takes the oracle's
+        b = np.searchsorted(cu, np.arange(len(out)), side="right") - 1
+        outside = (b < 0) | (b >= len(cu) - 1)
+        raw[outside] = ref_raw[outside]
     errs = check_rows(x_bits, dtype, base, n, k, raw, ref_raw)
     want = oracle.page1_translate(raw, pt, cu)
     if not np.array_equal(out, want):
@@ -174,4 +200,47 @@ def test_page1_dtypes_narrow_table(dtype):
     say(f"page-size-1 transform dtype {dtype}")
     out, raw = _run_page1(x, dtype, W, lengths, starts, pt, cu, k, offset=3)
     errs = _check_page1(x, dtype, W, lengths, starts, pt, cu, k, out, raw)
+    assert errs == [], "\n".join(errs)
+
+
+# ---------------------------------------------------------------------------
+# both transforms through every internal path, forced, on a reduced page batch
+# ---------------------------------------------------------------------------
+
+FORCED = {
+    "careful": dict(force=1),
+    "fallback": dict(force=2),
+    "spill": dict(lds=64),
+    "overflow": dict(lds=64, spill=64),
+    "split8_spill": dict(nsplit=8, min_chunk=1024, lds=64),
+    "split3_fallback": dict(nsplit=3, min_chunk=4096, force=2),
+}
+
+
+@pytest.mark.parametrize("with_raw", [True, False])
+@pytest.mark.parametrize("path", sorted(FORCED))
+def test_page1_forced_paths(path, with_raw):
+    wl = workloads.make("page", rows=24)
+    rng = np.random.default_rng(71)
+    cu = _requests(rng, wl.rows)
+    B = len(cu) - 1
+    pt = np.stack([rng.permutation(1 << 20)[: wl.width] for _ in range(B)]).astype(np.int32)
+    say(f"page-size-1 transform {path} raw={with_raw}")
+    out, raw = _run_page1(wl.x, wl.dtype, wl.width, wl.lengths, wl.row_starts, pt, cu, wl.k,
+                          FORCED[path], with_raw=with_raw)
+    assert (raw is None) == (not with_raw)
+    errs = _check_page1(wl.x, wl.dtype, wl.width, wl.lengths, wl.row_starts, pt, cu, wl.k, out, raw)
+    assert errs == [], "\n".join(errs)
+
+
+@pytest.mark.parametrize("with_raw", [True, False])
+@pytest.mark.parametrize("path", sorted(FORCED))
+def test_ragged_forced_paths(path, with_raw):
+    wl = workloads.make("page", rows=24)
+    offsets = np.random.default_rng(72).integers(0, 1 << 28, size=wl.rows).astype(np.int32)
+    say(f"ragged transform {path} raw={with_raw}")
+    with tuning(**FORCED[path]):
+        out, raw = _run(wl.x, wl.dtype, wl.width, wl.lengths, wl.row_starts, offsets, wl.k,
+                        with_raw=with_raw)
+    errs = _check(wl.x, wl.dtype, wl.width, wl.lengths, wl.row_starts, offsets, wl.k, out, raw)
     assert errs == [], "\n".join(errs)
