@@ -5,6 +5,7 @@
  * with ties interchangeable:
  *
  *   vts_topk_varlen                 decode-step top-k with per-request lengths
+ *   vts_topk_varlen_ordered         the same in canonical order with a tie-break
  *   vts_topk_page_table_transform   top-k over row windows, fused with a
  *                                   page-table translation of the indices
  *
@@ -114,6 +115,37 @@ int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t
                     int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
                     int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
                     void* out_values, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tie-breaks of vts_topk_varlen_ordered. */
+enum vts_tie_break {
+    VTS_TIE_SMALL = 1, /* of the values equal to the k-th, the smallest columns */
+    VTS_TIE_LARGE = 2  /* of the values equal to the k-th, the largest columns */
+};
+
+/*
+ * vts_topk_varlen_ordered -- vts_topk_varlen in deterministic mode (the
+ * FlashInfer page-size PR body on the SGLang PR #33237 page, "Description" and
+ * "Performance": a deterministic post-sort of each row's outputs and a SMALL /
+ * LARGE choice among tied values).  The order itself is not spelled out there;
+ * value descending, then column ascending, is the reading taken here.
+ *
+ * Arguments, windows, errors and workspace are those of vts_topk_varlen;
+ * tie_break is VTS_TIE_SMALL or VTS_TIE_LARGE (else VTS_ERR_INVALID).  The
+ * selected set is unique: every value above the k-th largest, then, of the
+ * values equal to it, those at the smallest (SMALL) or largest (LARGE)
+ * columns.  Each row's outputs are in canonical order: value descending, then
+ * column ascending; a row with n <= top_k lists all n columns in that order,
+ * then -1.  The output is a function of the inputs alone (bit-identical from
+ * run to run).  Values are ordered by the bits' total order: -0 ranks just
+ * below +0 here (vts_topk_varlen treats them as ties), NaN with the sign clear
+ * above +inf and with the sign set below -inf.  The sort adds an epilogue per
+ * row (about 66 LDS compare-exchange rounds at top_k 2048).
+ */
+int vts_topk_varlen_ordered(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                            int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
+                            int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
+                            int32_t* out_indices, void* out_values, void* workspace,
+                            size_t workspace_bytes, void* stream, int32_t tie_break);
 
 /*
  * vts_topk_page_table_transform -- top-k over row windows with the compact

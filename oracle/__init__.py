@@ -226,6 +226,67 @@ def topk_varlen(logits: np.ndarray, dtype: int, seq_lens: np.ndarray, k: int, ne
     return idx, vals, n
 
 
+def _as_float(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Raw element bits -> float64 values."""
+    if dtype == F32:
+        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    if dtype == BF16:
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+
+
+def select_ordered(x: np.ndarray, dtype: int, base: np.ndarray, n: np.ndarray, k: int, tie: str,
+                   return_values: bool = False, nthreads: int | None = None):
+    """Deterministic mode (FlashInfer page-size PR body on the SGLang PR #33237
+    page, "Description" and "Performance": a post-sort of the outputs and a
+    SMALL/LARGE choice among tied values).  Every value above the k-th largest,
+    then, of those equal to it, the ones at the smallest ("small") or largest
+    ("large") columns; each row listed by value descending, then column
+    ascending.
+
+    "small" takes `select` itself, whose full sort already orders ties by
+    ascending column.  "large" runs `select` on each window reversed (column j
+    read as n - 1 - j), so its tie order favours the largest original columns,
+    and maps the columns back.  Both then sort each row's entries by value
+    descending, column ascending (rows with n <= k come from `select` in column
+    order: every column, then -1).  Values compare as numbers (-0 equals +0);
+    the ordered kernel ranks -0 below +0, so inputs with zeros or NaN are not
+    covered by this oracle.
+    """
+    assert tie in ("small", "large")
+    R = x.shape[0]
+    n = np.asarray(n, np.int64)
+    base = np.asarray(base, np.int64)
+    if tie == "small":
+        idx, vals = select(x, dtype, base, n, k, True, nthreads)
+    else:
+        wmax = max(int(n.max()) if R else 0, 1)
+        xr = np.zeros((R, wmax), x.dtype)
+        for r in range(R):
+            m = int(n[r])
+            if m:
+                xr[r, :m] = x[r, base[r]:base[r] + m][::-1]
+        idx_r, vals = select(xr, dtype, np.zeros(R, np.int64), n, k, True, nthreads)
+        idx = np.where(idx_r < 0, -1, (n[:, None] - 1 - idx_r)).astype(np.int32)
+    for r in range(R):
+        m = min(int(n[r]), k)
+        v = _as_float(vals[r, :m], dtype)
+        order = np.lexsort((idx[r, :m], -v))  # value descending, then column ascending
+        idx[r, :m] = idx[r, :m][order]
+        vals[r, :m] = vals[r, :m][order]
+    return idx, (vals if return_values else None)
+
+
+def topk_varlen_ordered(logits: np.ndarray, dtype: int, seq_lens: np.ndarray, k: int, tie: str,
+                        next_n: int = 1, compress_ratio: int = 1, return_values: bool = False,
+                        nthreads: int | None = None):
+    """Oracle of topk_varlen_ordered: (idx, values-or-None, n per row)."""
+    R, W = logits.shape
+    base, n = varlen_rows(seq_lens, R, next_n, compress_ratio, W)
+    idx, vals = select_ordered(logits, dtype, base, n, k, tie, return_values, nthreads)
+    return idx, vals, n
+
+
 def topk_page_table_transform(scores: np.ndarray, dtype: int, lengths: np.ndarray, row_starts,
                               page_table: np.ndarray, page_table_row_starts, page_size: int, k: int,
                               nthreads: int | None = None):

@@ -49,8 +49,9 @@ def tuning(**kw):
 
 
 def run_varlen(wl, use_hint: bool = True, offset: int = 0, canary: bool = True,
-               return_values: bool | None = None):
-    """Runs topk_varlen on the GPU; returns (idx, vals or None, stats) as numpy."""
+               return_values: bool | None = None, tie: str | None = None):
+    """Runs topk_varlen (topk_varlen_ordered with `tie`) on the GPU; returns
+    (idx, vals or None, stats) as numpy."""
     x = to_device_scores(wl.x, wl.dtype, wl.width, offset)
     seq = torch.from_numpy(wl.seq_lens).cuda()
     rv = wl.return_values if return_values is None else return_values
@@ -67,9 +68,12 @@ def run_varlen(wl, use_hint: bool = True, offset: int = 0, canary: bool = True,
     if use_hint and wl.pre_idx is not None:
         hint = torch.from_numpy(wl.pre_idx).cuda()
     ws = vts.make_workspace(R, wl.width, k, TORCH_DTYPE[wl.dtype], "cuda")
-    idx, vals = vts.topk_varlen(x, seq, k, pre_idx=hint, compress_ratio=wl.compress_ratio,
-                                next_n=wl.next_n, return_values=rv, out_indices=out_idx,
-                                out_values=out_vals, workspace=ws)
+    kw = dict(pre_idx=hint, compress_ratio=wl.compress_ratio, next_n=wl.next_n, return_values=rv,
+              out_indices=out_idx, out_values=out_vals, workspace=ws)
+    if tie is None:
+        idx, vals = vts.topk_varlen(x, seq, k, **kw)
+    else:
+        idx, vals = vts.topk_varlen_ordered(x, seq, k, tie_break=tie, **kw)
     torch.cuda.synchronize()
     stats = vts.workspace_stats(ws)
     # self-restoring workspace: every ticket is back to zero

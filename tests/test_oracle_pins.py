@@ -437,3 +437,58 @@ def test_transform_checker_rejects_bad_translation():
     bad = out.copy()
     bad[0, 3] += 1
     assert check_transform(x, F32, base, n, k, bad, raw, raw, pt, ptrs, ps) != []
+
+
+# ---------------------------------------------------------------------------
+# deterministic mode: canonical order and the SMALL / LARGE tie-break
+# ---------------------------------------------------------------------------
+
+def _ordered_cases():
+    for line in open(os.path.join(GOLDEN, "ordered_ties.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        head, vals, want = (part.split() for part in line.split("|"))
+        yield head[0], int(head[1]), [float(v) for v in vals], [int(w) for w in want]
+
+
+@pytest.mark.parametrize("case", list(_ordered_cases()), ids=lambda c: f"{c[0]}-k{c[1]}-{len(c[2])}")
+def test_ordered_hand_table(case):
+    tie, k, vals, want = case
+    x = np.array([vals], np.float32).view(np.uint32)
+    idx, v, _ = oracle.topk_varlen_ordered(x, F32, np.array([len(vals)], np.int32), k, tie,
+                                           return_values=True)
+    assert idx[0].tolist() == want
+    got = [vals[j] for j in want if j >= 0]
+    assert v[0][:len(got)].view(np.float32).tolist() == got
+
+
+@pytest.mark.parametrize("tie", ["small", "large"])
+def test_ordered_brute_force_subsets(tie):
+    """Every k-subset of tiny rows with many ties: the valid top-k subsets are
+    those whose smallest value is >= every value left out; "small" is the one
+    with the least column sum, "large" the greatest (they differ only in which
+    tied columns they hold).  The output lists it by value descending, then
+    column ascending."""
+    rng = np.random.default_rng(5 if tie == "small" else 6)
+    for _ in range(150):
+        n = int(rng.integers(1, 8))
+        k = int(rng.integers(1, 8))
+        vals = rng.integers(-2, 3, size=n).astype(np.float32)
+        vals[vals == 0] = 0.5  # no zeros: the ordered mode orders -0 below +0
+        x = vals.view(np.uint32)[None, :]
+        idx, _, _ = oracle.topk_varlen_ordered(x, F32, np.array([n], np.int32), k, tie)
+        m = min(n, k)
+        best = None
+        for sub in itertools.combinations(range(n), m):
+            rest = [j for j in range(n) if j not in sub]
+            if rest and min(vals[list(sub)]) < max(vals[rest]):
+                continue
+            key = sum(sub) if tie == "small" else -sum(sub)
+            if best is None or key < best[0]:
+                best = (key, sub)
+        chosen = sorted(best[1])
+        got = [j for j in idx[0].tolist() if j >= 0]
+        assert sorted(got) == chosen, (vals, k, got, chosen)
+        assert idx[0].tolist()[m:] == [-1] * (k - m)
+        for a, b in zip(got, got[1:]):
+            assert vals[a] > vals[b] or (vals[a] == vals[b] and a < b), (vals, got)

@@ -21,7 +21,7 @@ import warnings
 
 import torch
 
-__all__ = ["topk_varlen", "topk_page_table_transform", "topk_transform_ragged",
+__all__ = ["topk_varlen", "topk_varlen_ordered", "topk_page_table_transform", "topk_transform_ragged",
            "topk_transform_page1",
            "workspace_bytes", "make_workspace",
            "set_tuning", "workspace_stats", "VtsError", "library", "LIB_PATH"]
@@ -58,6 +58,9 @@ def library():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.vts_topk_varlen.restype = ctypes.c_int
     lib.vts_topk_varlen.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.vts_topk_varlen_ordered.restype = ctypes.c_int
+    lib.vts_topk_varlen_ordered.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp,
+                                            vp, sz, vp, i32]
     lib.vts_topk_transform_page1.restype = ctypes.c_int
     lib.vts_topk_transform_page1.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i64, i64, vp, i64,
                                              i32, vp, vp, vp, sz, vp]
@@ -165,6 +168,30 @@ def topk_varlen(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
                 out_values: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
                 stream=None):
     """Exact top-k of each row's valid prefix (see vts_topk_varlen in include/vts.h)."""
+    return _varlen(logits, seq_lens, top_k, pre_idx, compress_ratio, next_n, return_values,
+                   out_indices, out_values, workspace, stream, None)
+
+
+TIE_BREAK = {"small": 1, "large": 2}
+
+
+def topk_varlen_ordered(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
+                        tie_break: str = "small", pre_idx: torch.Tensor | None = None,
+                        compress_ratio: int = 1, next_n: int = 1, return_values: bool = False,
+                        out_indices: torch.Tensor | None = None,
+                        out_values: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None, stream=None):
+    """topk_varlen in canonical order (value descending, column ascending) with
+    the ties at the k-th value taken at the smallest or largest columns (see
+    vts_topk_varlen_ordered in include/vts.h)."""
+    if tie_break not in TIE_BREAK:
+        raise ValueError(f"tie_break must be one of {sorted(TIE_BREAK)}")
+    return _varlen(logits, seq_lens, top_k, pre_idx, compress_ratio, next_n, return_values,
+                   out_indices, out_values, workspace, stream, TIE_BREAK[tie_break])
+
+
+def _varlen(logits, seq_lens, top_k, pre_idx, compress_ratio, next_n, return_values, out_indices,
+            out_values, workspace, stream, tie):
     _check_scores(logits, "logits")
     R, W = logits.shape
     dev = logits.device
@@ -181,11 +208,15 @@ def topk_varlen(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
     sp = _stream_ptr(stream, dev)
     if workspace is None:
         workspace = _default_workspace(workspace_bytes(R, W, top_k, logits.dtype), dev, sp)
-    st = library().vts_topk_varlen(
-        logits.data_ptr(), _DTYPE[logits.dtype], R, W, logits.stride(0) if R > 1 else W,
-        seq_lens.data_ptr(), top_k, next_n, compress_ratio, _ptr(pre_idx), idx.data_ptr(),
-        _ptr(vals), workspace.data_ptr(), workspace.numel(), sp)
-    _check("vts_topk_varlen", st)
+    args = (logits.data_ptr(), _DTYPE[logits.dtype], R, W, logits.stride(0) if R > 1 else W,
+            seq_lens.data_ptr(), top_k, next_n, compress_ratio, _ptr(pre_idx), idx.data_ptr(),
+            _ptr(vals), workspace.data_ptr(), workspace.numel(), sp)
+    if tie is None:
+        st = library().vts_topk_varlen(*args)
+        _check("vts_topk_varlen", st)
+    else:
+        st = library().vts_topk_varlen_ordered(*args, tie)
+        _check("vts_topk_varlen_ordered", st)
     if st == WARN_HINT_DISCARDED:
         warnings.warn("pre_idx unusable; ran without a hint", RuntimeWarning)
     return idx, vals

@@ -146,10 +146,11 @@ int vts_workspace_init(void* workspace, size_t bytes, void* stream) {
     return VTS_OK;
 }
 
-int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
-                    int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
-                    int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
-                    void* out_values, void* workspace, size_t workspace_bytes_, void* stream) {
+static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                            int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
+                            int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
+                            int32_t* out_indices, void* out_values, void* workspace,
+                            size_t workspace_bytes_, void* stream, int32_t order) {
     int st = check_rows(logits, dtype, num_rows, width, row_stride, top_k);
     if (st != VTS_OK) return st;
     if (next_n < 1 || compress_ratio < 1 || num_rows % next_n != 0) return VTS_ERR_INVALID;
@@ -183,9 +184,31 @@ int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t
     p.pre_idx = pre_idx;
     p.out_idx = out_indices;
     p.out_vals = out_values;
+    p.order = order;
     fill_plan(p, num_rows, width, workspace);
     if (launch_varlen(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess) return VTS_ERR_HIP;
     return warn;
+}
+
+int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                    int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
+                    int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
+                    void* out_values, void* workspace, size_t workspace_bytes_, void* stream) {
+    return topk_varlen_impl(logits, dtype, num_rows, width, row_stride, seq_lens, top_k, next_n,
+                            compress_ratio, pre_idx, out_indices, out_values, workspace,
+                            workspace_bytes_, stream, ORDER_ANY);
+}
+
+int vts_topk_varlen_ordered(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                            int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
+                            int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
+                            int32_t* out_indices, void* out_values, void* workspace,
+                            size_t workspace_bytes_, void* stream, int32_t tie_break) {
+    if (tie_break != VTS_TIE_SMALL && tie_break != VTS_TIE_LARGE) return VTS_ERR_INVALID;
+    return topk_varlen_impl(logits, dtype, num_rows, width, row_stride, seq_lens, top_k, next_n,
+                            compress_ratio, pre_idx, out_indices, out_values, workspace,
+                            workspace_bytes_, stream,
+                            tie_break == VTS_TIE_SMALL ? ORDER_SMALL : ORDER_LARGE);
 }
 
 int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows,

@@ -22,6 +22,10 @@ constexpr int BALANCE_XCDS = 8;
 constexpr int BALANCE_CUS_PER_XCD = 32;
 constexpr int BALANCE_CUS = BALANCE_XCDS * BALANCE_CUS_PER_XCD;
 
+// Output order: any (fastest), or canonical (value descending, column
+// ascending) with the boundary ties taken at the smallest or largest columns.
+constexpr int ORDER_ANY = 0, ORDER_SMALL = 1, ORDER_LARGE = 2;
+
 struct Params {
     // score rows
     const void* x;
@@ -57,6 +61,7 @@ struct Params {
     int32_t lds_cap;    // on-chip candidate slots used before spilling (<= CAP)
     int32_t hi_cap;     // candidate slots in all (<= HI_SLOTS) before re-filtering
     int32_t force_path;
+    int32_t order;      // ORDER_ANY, or canonical order with a tie-break (ORDER_SMALL/LARGE)
     float sigma;        // margin of the safe rung, in standard deviations
     float sigma2;       // margin of the likely rung (<= sigma)
     // workspace

@@ -149,6 +149,12 @@ struct PagePolicy {
         const int64_t page = gload(p.pt + (int64_t)r * p.pt_stride + pc);
         return (int32_t)(page * p.page_size + col % p.page_size);
     }
+    template <int DT>
+    __device__ __forceinline__ static void emit(const Params& p, int r, int64_t base, uint32_t pos, int32_t col,
+                                                uint32_t) {
+        put_raw(p, r, pos, col);
+        put_idx(p, r, pos, translate(p, r, row(p, r, base), col));
+    }
     // output slot pos: the raw index col, and the translated index t
     __device__ __forceinline__ static void put_raw(const Params& p, int r, uint32_t pos, int32_t col) {
         if (p.out_raw) gstore(p.out_raw + (int64_t)r * p.k + pos, col);
@@ -968,6 +974,82 @@ struct LdsSrc {
     }
 };
 
+// Canonical order: sorts LDS slots [0, m) by key descending, then column
+// ascending (a bitonic network over the next power of two, padding slots
+// sorting last), and writes the first m through the policy, then -1 / pad
+// values up to k.
+static_assert(CAP >= 2048, "a canonical-order sort of up to 2048 entries fits the candidate slots");
+
+template <int DT, class Policy>
+__device__ __forceinline__ void sort_and_emit(Smem& sm, const Params& p, int r, int64_t base, uint32_t m) {
+    uint32_t P = 1;
+    while (P < m) P <<= 1;
+    for (uint32_t q = m + threadIdx.x; q < P; q += NT) {
+        sm.key[q] = 0u;
+        sm.idx[q] = 0xFFFFFFFFu;  // complement 0: below every column of a key-0 entry
+    }
+    lds_sync();
+    for (uint32_t size = 2; size <= P; size <<= 1) {
+        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
+            for (uint32_t t = threadIdx.x; t < P / 2; t += NT) {
+                const uint32_t i = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
+                const uint32_t j = i + stride;
+                const uint64_t a = ((uint64_t)sm.key[i] << 32) | (uint32_t)~sm.idx[i];
+                const uint64_t b = ((uint64_t)sm.key[j] << 32) | (uint32_t)~sm.idx[j];
+                const bool down = (i & size) == 0;  // this block ends descending
+                if (down ? a < b : a > b) {
+                    const uint32_t ki = sm.key[i], ii = sm.idx[i];
+                    sm.key[i] = sm.key[j];
+                    sm.idx[i] = sm.idx[j];
+                    sm.key[j] = ki;
+                    sm.idx[j] = ii;
+                }
+            }
+            lds_sync();
+        }
+    }
+    for (uint32_t q = threadIdx.x; q < (uint32_t)p.k; q += NT) {
+        const bool in = q < m;
+        Policy::template emit<DT>(p, r, base, q, in ? (int32_t)sm.idx[q] : -1,
+                                  in ? from_key<DT>(sm.key[q]) : Traits<DT>::PAD);
+    }
+}
+
+// Canonical order for a row with more than k candidates: of the keys equal to
+// the k-th key K, the k - gt with the smallest (ORDER_SMALL) or largest
+// (ORDER_LARGE) columns are taken (a second exact select over their columns,
+// which are distinct), the k winners are gathered into LDS and sorted.
+template <int DT, class Policy, class Src>
+__device__ __forceinline__ void ordered_emit(Smem& sm, const Params& p, int r, int64_t base,
+                                             const Src& src, uint32_t K, uint32_t gt) {
+    const uint32_t need_eq = (uint32_t)p.k - gt;
+    const bool small = p.order == ORDER_SMALL;
+    uint32_t C, cgt;
+    block_select_exact(
+        sm,
+        [&](auto f) {
+            src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+                if (ok && key == K) f(small ? ~col : col);
+            });
+        },
+        need_eq, C, cgt);
+    if (threadIdx.x == 0) sm.cnt_a = 0;
+    lds_sync();
+    uint32_t nsel = 0;
+    src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+        nsel += (ok && (key > K || (key == K && (small ? ~col : col) >= C))) ? 1u : 0u;
+    });
+    uint32_t o = wave_ticket_n(&sm.cnt_a, nsel);
+    src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+        if (ok && (key > K || (key == K && (small ? ~col : col) >= C))) {
+            sm.key[o] = key;
+            sm.idx[o] = col;
+            ++o;
+        }
+    });
+    sort_and_emit<DT, Policy>(sm, p, r, base, (uint32_t)p.k);
+}
+
 // Selects the top k of `src` (which must hold at least k entries and contain
 // a top-k of the row) and writes them through the policy.
 template <int DT, class Policy, class Src>
@@ -981,6 +1063,10 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
             });
         },
         (uint32_t)p.k, K, gt);
+    if (p.order != ORDER_ANY) {
+        ordered_emit<DT, Policy>(sm, p, r, base, src, K, gt);
+        return;
+    }
     const uint32_t need_eq = (uint32_t)p.k - gt;
     if (threadIdx.x == 0) {
         sm.cnt_a = 0;
@@ -1231,7 +1317,19 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     n = __builtin_amdgcn_readfirstlane((int)n);
     const raw_t* row = static_cast<const raw_t*>(p.x) + (int64_t)r * p.row_stride + base;
     if (n <= p.k) {
-        if (c == 0) short_row<DT, Policy>(p, r, base, n, row);
+        if (c == 0) {
+            if (p.order != ORDER_ANY) {
+                // every column is selected; canonical order sorts them
+                lds_sync();
+                for (int j = threadIdx.x; j < n; j += NT) {
+                    sm.key[j] = to_key<DT>((uint32_t)gload(row + j));
+                    sm.idx[j] = (uint32_t)j;
+                }
+                sort_and_emit<DT, Policy>(sm, p, r, base, (uint32_t)n);
+            } else {
+                short_row<DT, Policy>(p, r, base, n, row);
+            }
+        }
         return;
     }
     int64_t eff64 = (n + p.min_chunk - 1) / p.min_chunk;
