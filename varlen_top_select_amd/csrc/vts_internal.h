@@ -61,7 +61,6 @@ struct Params {
     int32_t lds_cap;    // on-chip candidate slots used before spilling (<= CAP)
     int32_t hi_cap;     // candidate slots in all (<= HI_SLOTS) before re-filtering
     int32_t force_path;
-    int32_t order;      // ORDER_ANY, or canonical order with a tie-break (ORDER_SMALL/LARGE)
     float sigma;        // margin of the safe rung, in standard deviations
     float sigma2;       // margin of the likely rung (<= sigma)
     // workspace
@@ -71,6 +70,7 @@ struct Params {
     uint32_t* ws_count_up;  // of which keys >= the likely rung, per unit
     uint32_t* ws_key;
     uint32_t* ws_idx;
+    int32_t order;  // ORDER_ANY, or canonical order with a tie-break (ORDER_SMALL/LARGE)
 };
 
 enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };

@@ -51,6 +51,8 @@ namespace vts {
 struct VarlenPolicy {
     // the output needs no memory reads of its own
     static constexpr bool GATHERS = false;
+    // outputs in any order (OrderedVarlenPolicy: canonical order)
+    static constexpr bool ORDERED = false;
     // FlashInfer top_k_varlen doc, `seq_lens`: row t of request i ranks its
     // first max(0, (seq_lens[i] - next_n + t + 1) // compress_ratio) columns,
     // clamped to the width.
@@ -84,9 +86,16 @@ struct VarlenPolicy {
     }
 };
 
+// The deterministic mode of the varlen selection: its own kernels, so the
+// sort and the tie-break select add no code to the unordered ones.
+struct OrderedVarlenPolicy : VarlenPolicy {
+    static constexpr bool ORDERED = true;
+};
+
 struct PagePolicy {
     // each output index is read from a table (or an offset) in memory
     static constexpr bool GATHERS = true;
+    static constexpr bool ORDERED = false;
     // Window [row_start, row_start + n), n = clamp(length, 0, width - row_start);
     // a start outside [0, width] is an empty row.
     struct Raw {
@@ -148,12 +157,6 @@ struct PagePolicy {
         if (pc < 0 || pc >= p.pt_width) return -1;
         const int64_t page = gload(p.pt + (int64_t)r * p.pt_stride + pc);
         return (int32_t)(page * p.page_size + col % p.page_size);
-    }
-    template <int DT>
-    __device__ __forceinline__ static void emit(const Params& p, int r, int64_t base, uint32_t pos, int32_t col,
-                                                uint32_t) {
-        put_raw(p, r, pos, col);
-        put_idx(p, r, pos, translate(p, r, row(p, r, base), col));
     }
     // output slot pos: the raw index col, and the translated index t
     __device__ __forceinline__ static void put_raw(const Params& p, int r, uint32_t pos, int32_t col) {
@@ -1063,7 +1066,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
             });
         },
         (uint32_t)p.k, K, gt);
-    if (p.order != ORDER_ANY) {
+    if constexpr (Policy::ORDERED) {
         ordered_emit<DT, Policy>(sm, p, r, base, src, K, gt);
         return;
     }
@@ -1318,7 +1321,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const raw_t* row = static_cast<const raw_t*>(p.x) + (int64_t)r * p.row_stride + base;
     if (n <= p.k) {
         if (c == 0) {
-            if (p.order != ORDER_ANY) {
+            if constexpr (Policy::ORDERED) {
                 // every column is selected; canonical order sorts them
                 lds_sync();
                 for (int j = threadIdx.x; j < n; j += NT) {
@@ -1591,6 +1594,14 @@ static hipError_t launch_dt(const Params& p, hipStream_t stream) {
 }
 
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream) {
+    if (p.order != ORDER_ANY) {
+        switch (dtype) {
+            case F32: return launch_dt<F32, OrderedVarlenPolicy>(p, stream);
+            case BF16: return launch_dt<BF16, OrderedVarlenPolicy>(p, stream);
+            case F16: return launch_dt<F16, OrderedVarlenPolicy>(p, stream);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (dtype) {
         case F32: return launch_dt<F32, VarlenPolicy>(p, stream);
         case BF16: return launch_dt<BF16, VarlenPolicy>(p, stream);
