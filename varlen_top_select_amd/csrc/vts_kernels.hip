@@ -1593,15 +1593,10 @@ static hipError_t launch_dt(const Params& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+static hipError_t launch_varlen_ordered(int dtype, const Params& p, hipStream_t stream);
+
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream) {
-    if (p.order != ORDER_ANY) {
-        switch (dtype) {
-            case F32: return launch_dt<F32, OrderedVarlenPolicy>(p, stream);
-            case BF16: return launch_dt<BF16, OrderedVarlenPolicy>(p, stream);
-            case F16: return launch_dt<F16, OrderedVarlenPolicy>(p, stream);
-        }
-        return hipErrorInvalidValue;
-    }
+    if (p.order != ORDER_ANY) return launch_varlen_ordered(dtype, p, stream);
     switch (dtype) {
         case F32: return launch_dt<F32, VarlenPolicy>(p, stream);
         case BF16: return launch_dt<BF16, VarlenPolicy>(p, stream);
@@ -1643,6 +1638,17 @@ hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream) {
         case F32: return launch_dt<F32, PagePolicy>(p, stream);
         case BF16: return launch_dt<BF16, PagePolicy>(p, stream);
         case F16: return launch_dt<F16, PagePolicy>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+// Defined last, so the deterministic-mode kernels follow the others in the
+// code object and leave the unordered kernels where they were.
+static hipError_t launch_varlen_ordered(int dtype, const Params& p, hipStream_t stream) {
+    switch (dtype) {
+        case F32: return launch_dt<F32, OrderedVarlenPolicy>(p, stream);
+        case BF16: return launch_dt<BF16, OrderedVarlenPolicy>(p, stream);
+        case F16: return launch_dt<F16, OrderedVarlenPolicy>(p, stream);
     }
     return hipErrorInvalidValue;
 }
