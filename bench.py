@@ -65,7 +65,7 @@ def _code_only(text: str) -> str:
     return re.sub(r"\s+", "", text)
 
 
-KERNEL_SOURCES = ("vts_device.hpp", "vts_internal.h", "vts_kernels.hip")
+KERNEL_SOURCES = ("vts_device.hpp", "vts_internal.h", "vts_topk.hpp", "vts_kernels.hip")
 
 
 def kernel_source_hash(csrc: str | None = None) -> str:

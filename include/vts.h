@@ -116,10 +116,14 @@ int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t
                     int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
                     void* out_values, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Tie-breaks of vts_topk_varlen_ordered. */
+/* Tie-breaks of the deterministic mode (the *_ordered entry points). */
 enum vts_tie_break {
-    VTS_TIE_SMALL = 1, /* of the values equal to the k-th, the smallest columns */
-    VTS_TIE_LARGE = 2  /* of the values equal to the k-th, the largest columns */
+    VTS_TIE_SMALL = 1,   /* of the values equal to the k-th, the smallest columns */
+    VTS_TIE_LARGE = 2,   /* of the values equal to the k-th, the largest columns */
+    /* added to SMALL or LARGE: the same selected set, written in no particular
+     * order (no canonical sort); a row with n <= top_k is then the identity
+     * 0..n-1 followed by -1, as in the unordered entry points */
+    VTS_TIE_UNSORTED = 4
 };
 
 /*
@@ -130,16 +134,20 @@ enum vts_tie_break {
  * value descending, then column ascending, is the reading taken here.
  *
  * Arguments, windows, errors and workspace are those of vts_topk_varlen;
- * tie_break is VTS_TIE_SMALL or VTS_TIE_LARGE (else VTS_ERR_INVALID).  The
- * selected set is unique: every value above the k-th largest, then, of the
- * values equal to it, those at the smallest (SMALL) or largest (LARGE)
- * columns.  Each row's outputs are in canonical order: value descending, then
- * column ascending; a row with n <= top_k lists all n columns in that order,
- * then -1.  The output is a function of the inputs alone (bit-identical from
- * run to run).  Values are ordered by the bits' total order: -0 ranks just
- * below +0 here (vts_topk_varlen treats them as ties), NaN with the sign clear
- * above +inf and with the sign set below -inf.  The sort adds an epilogue per
- * row (about 66 LDS compare-exchange rounds at top_k 2048).
+ * tie_break is VTS_TIE_SMALL or VTS_TIE_LARGE, optionally plus
+ * VTS_TIE_UNSORTED (anything else: VTS_ERR_INVALID).  The selected set is
+ * unique: every value above the k-th largest, then, of the values equal to
+ * it, those at the smallest (SMALL) or largest (LARGE) columns.  Values
+ * compare as numbers: -0 and +0 are equal (TensorRT-LLM PR #17821, "Test
+ * coverage": signed zeros normalised), every NaN with the sign clear is
+ * above +inf and equal to every other such NaN, every NaN with the sign set
+ * below -inf and equal to every other such NaN.  Each row's outputs are in
+ * canonical order: value descending, then column ascending; a row with
+ * n <= top_k lists all n columns in that order, then -1.  The output is a
+ * function of the inputs alone (bit-identical from run to run); out_values
+ * are bit copies of the selected elements, as for vts_topk_varlen.  The sort
+ * adds an epilogue per row (about 66 LDS compare-exchange rounds at top_k
+ * 2048); VTS_TIE_UNSORTED skips it.
  */
 int vts_topk_varlen_ordered(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
                             int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
@@ -188,6 +196,21 @@ int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num
                                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * vts_topk_page_table_transform_ordered -- vts_topk_page_table_transform in
+ * the deterministic mode of vts_topk_varlen_ordered (same page, "Description":
+ * `out_raw_indices` stays positionally aligned with `out` through the
+ * deterministic post-sort).  The selection over each window, its order and
+ * tie_break are those of vts_topk_varlen_ordered, on window-relative indices;
+ * `out` holds their translations slot by slot.
+ */
+int vts_topk_page_table_transform_ordered(
+    const void* scores, int32_t dtype, int64_t num_rows, int64_t width, int64_t row_stride,
+    const int32_t* lengths, const int32_t* row_starts, const int32_t* src_page_table,
+    int64_t page_table_stride, int64_t page_table_width, const int32_t* page_table_row_starts,
+    int32_t page_size, int32_t top_k, int32_t* out, int32_t* out_raw_indices, void* workspace,
+    size_t workspace_bytes, void* stream, int32_t tie_break);
+
+/*
  * vts_topk_transform_ragged -- top-k over row windows with the ragged-KV index
  * transform (SGLang TopK_Ops page, fast_topk_transform_ragged_fused: the
  * offset of each row's top-k indices in a ragged KV buffer).
@@ -210,6 +233,15 @@ int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_row
                               const int32_t* row_starts, const int32_t* topk_indices_offset,
                               int32_t top_k, int32_t* out, int32_t* out_raw_indices,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* vts_topk_transform_ragged in the deterministic mode (see
+ * vts_topk_page_table_transform_ordered). */
+int vts_topk_transform_ragged_ordered(const void* scores, int32_t dtype, int64_t num_rows,
+                                      int64_t width, int64_t row_stride, const int32_t* lengths,
+                                      const int32_t* row_starts,
+                                      const int32_t* topk_indices_offset, int32_t top_k,
+                                      int32_t* out, int32_t* out_raw_indices, void* workspace,
+                                      size_t workspace_bytes, void* stream, int32_t tie_break);
 
 /*
  * vts_topk_transform_page1 -- top-k over row windows with the page-size-1
@@ -241,6 +273,17 @@ int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows
                              int64_t num_batches, int32_t top_k, int32_t* out,
                              int32_t* out_raw_indices, void* workspace, size_t workspace_bytes,
                              void* stream);
+
+/* vts_topk_transform_page1 in the deterministic mode (see
+ * vts_topk_page_table_transform_ordered). */
+int vts_topk_transform_page1_ordered(const void* scores, int32_t dtype, int64_t num_rows,
+                                     int64_t width, int64_t row_stride, const int32_t* lengths,
+                                     const int32_t* row_starts, const int32_t* page_table,
+                                     int64_t page_table_stride, int64_t page_table_width,
+                                     const int32_t* cu_seqlens_q, int64_t num_batches,
+                                     int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     int32_t tie_break);
 
 /* Aliases with the operation names of the pages. */
 int topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,

@@ -249,9 +249,11 @@ def select_ordered(x: np.ndarray, dtype: int, base: np.ndarray, n: np.ndarray, k
     read as n - 1 - j), so its tie order favours the largest original columns,
     and maps the columns back.  Both then sort each row's entries by value
     descending, column ascending (rows with n <= k come from `select` in column
-    order: every column, then -1).  Values compare as numbers (-0 equals +0);
-    the ordered kernel ranks -0 below +0, so inputs with zeros or NaN are not
-    covered by this oracle.
+    order: every column, then -1).  Values compare as `select` compares them:
+    as numbers, so -0 equals +0 (TensorRT-LLM PR #17821, "Test coverage":
+    signed zeros normalised), with every NaN whose sign bit is clear above
+    +inf and every NaN whose sign bit is set below -inf, NaNs of one sign
+    equal to each other.
     """
     assert tie in ("small", "large")
     R = x.shape[0]
@@ -268,10 +270,16 @@ def select_ordered(x: np.ndarray, dtype: int, base: np.ndarray, n: np.ndarray, k
                 xr[r, :m] = x[r, base[r]:base[r] + m][::-1]
         idx_r, vals = select(xr, dtype, np.zeros(R, np.int64), n, k, True, nthreads)
         idx = np.where(idx_r < 0, -1, (n[:, None] - 1 - idx_r)).astype(np.int32)
+    sign_shift = 31 if dtype == F32 else 15
     for r in range(R):
         m = min(int(n[r]), k)
         v = _as_float(vals[r, :m], dtype)
-        order = np.lexsort((idx[r, :m], -v))  # value descending, then column ascending
+        nan = np.isnan(v)
+        neg = (vals[r, :m].astype(np.uint64) >> sign_shift) & 1
+        cls = np.where(nan, np.where(neg == 1, -1, 1), 0)  # NaN sign class, 0 for numbers
+        v = np.where(nan, 0.0, v)
+        # NaN class descending, then value descending, then column ascending
+        order = np.lexsort((idx[r, :m], -v, -cls))
         idx[r, :m] = idx[r, :m][order]
         vals[r, :m] = vals[r, :m][order]
     return idx, (vals if return_values else None)
@@ -285,6 +293,44 @@ def topk_varlen_ordered(logits: np.ndarray, dtype: int, seq_lens: np.ndarray, k:
     base, n = varlen_rows(seq_lens, R, next_n, compress_ratio, W)
     idx, vals = select_ordered(logits, dtype, base, n, k, tie, return_values, nthreads)
     return idx, vals, n
+
+
+def _select_windows(scores, dtype, base, n, k, tie, nthreads):
+    """Window-relative top-k indices: `select`, or `select_ordered` with a tie."""
+    if tie is None:
+        return select(scores, dtype, base, n, k, False, nthreads)[0]
+    return select_ordered(scores, dtype, base, n, k, tie, False, nthreads)[0]
+
+
+def topk_page_table_transform_ordered(scores: np.ndarray, dtype: int, lengths: np.ndarray,
+                                      row_starts, page_table: np.ndarray, page_table_row_starts,
+                                      page_size: int, k: int, tie: str, nthreads: int | None = None):
+    """Oracle of the page transform in the deterministic mode: the ordered
+    selection of each window (`select_ordered`), translated slot by slot
+    (FlashInfer page-size PR body, "Description": `out_raw_indices` stays
+    aligned with `out` through the post-sort).  Returns (out, out_raw, base, n)."""
+    R, W = scores.shape
+    base, n = window_rows(lengths, row_starts, W)
+    raw = _select_windows(scores, dtype, base, n, k, tie, nthreads)
+    return page_translate(raw, page_table, page_table_row_starts, base, page_size), raw, base, n
+
+
+def topk_transform_ragged_ordered(scores, dtype, lengths, row_starts, offsets, k, tie,
+                                  nthreads=None):
+    """Oracle of the ragged transform in the deterministic mode: (out, out_raw, base, n)."""
+    R, W = scores.shape
+    base, n = window_rows(lengths, row_starts, W)
+    raw = _select_windows(scores, dtype, base, n, k, tie, nthreads)
+    return ragged_translate(raw, offsets), raw, base, n
+
+
+def topk_transform_page1_ordered(scores, dtype, lengths, row_starts, page_table, cu_seqlens_q, k,
+                                 tie, nthreads=None):
+    """Oracle of the page-size-1 transform in the deterministic mode: (out, out_raw, base, n)."""
+    R, W = scores.shape
+    base, n = window_rows(lengths, row_starts, W)
+    raw = _select_windows(scores, dtype, base, n, k, tie, nthreads)
+    return page1_translate(raw, page_table, cu_seqlens_q), raw, base, n
 
 
 def topk_page_table_transform(scores: np.ndarray, dtype: int, lengths: np.ndarray, row_starts,

@@ -17,7 +17,11 @@ A result is accepted when, for every checked row r with n valid columns:
 
 Which of several tied elements is chosen, and the order of the k slots, are
 not checked: the pages leave both open (ties interchangeable, no output order).
-NaN rows are outside parity: for them only (i) and (ii) are checked.
+Rows holding NaN are compared in the order the oracle documents (a NaN with
+the sign bit clear above +inf, one with it set below -inf, NaNs of one sign
+tied): (iii) and (iv) then compare (NaN sign class, value) pairs, so the count
+of NaNs of each sign that were selected and the multiset of the other
+selected values must equal the oracle's.
 """
 from __future__ import annotations
 
@@ -42,6 +46,17 @@ def raw_bits(x: np.ndarray, dtype: int) -> np.ndarray:
     if dtype == F32:
         return x.view(np.uint32) if x.dtype != np.uint32 else x
     return x.view(np.uint16) if x.dtype != np.uint16 else x
+
+
+def ranks(bits: np.ndarray, dtype: int) -> tuple[np.ndarray, np.ndarray]:
+    """(class, value) of each element in the oracle's order: class +1 for a
+    NaN with the sign bit clear, -1 for one with it set, 0 for numbers; value
+    0 for NaNs and -0 mapped to +0."""
+    v = decode(bits, dtype)
+    nan = np.isnan(v)
+    sign = (bits.astype(np.uint64) >> (31 if dtype == F32 else 15)) & 1
+    cls = np.where(nan, np.where(sign == 1, -1, 1), 0)
+    return cls, np.where(nan | (v == 0), 0.0, v)
 
 
 def check_rows(x: np.ndarray, dtype: int, base: np.ndarray, n: np.ndarray, k: int,
@@ -87,22 +102,29 @@ def check_rows(x: np.ndarray, dtype: int, base: np.ndarray, n: np.ndarray, k: in
             if np.any(gv[m:].astype(np.uint64) != pad):
                 errs.append(f"row {r}: padding values must be {pad:#x}")
                 continue
-        if nr <= k or np.isnan(wval).any():
+        if nr <= k:
             continue
-        sel = wval[head]
+        cls, val = ranks(wbits, dtype)
+
+        def sorted_pairs(cols):
+            o = np.lexsort((val[cols], cls[cols]))
+            return cls[cols][o], val[cols][o]
+
         if ref_idx is not None:
             ri = np.asarray(ref_idx[r], dtype=np.int64)[:m]
-            a = np.sort(np.where(sel == 0, 0.0, sel))
-            bref = wval[ri]
-            bb = np.sort(np.where(bref == 0, 0.0, bref))
-            if not np.array_equal(a, bb):
+            (ca, va), (cb, vb) = sorted_pairs(head), sorted_pairs(ri)
+            if not (np.array_equal(ca, cb) and np.array_equal(va, vb)):
                 errs.append(f"row {r}: selected value multiset differs from the oracle's")
                 continue
         mask = np.ones(nr, bool)
         mask[head] = False
-        if mask.any() and sel.min() < wval[mask].max():
-            errs.append(f"row {r}: a selected value is below an unselected one")
-            continue
+        if mask.any():
+            cs, vs = sorted_pairs(head)
+            rest = np.flatnonzero(mask)
+            cu, vu = sorted_pairs(rest)
+            if (cs[0], vs[0]) < (cu[-1], vu[-1]):
+                errs.append(f"row {r}: a selected value is below an unselected one")
+                continue
     return errs
 
 

@@ -49,9 +49,9 @@ def tuning(**kw):
 
 
 def run_varlen(wl, use_hint: bool = True, offset: int = 0, canary: bool = True,
-               return_values: bool | None = None, tie: str | None = None):
-    """Runs topk_varlen (topk_varlen_ordered with `tie`) on the GPU; returns
-    (idx, vals or None, stats) as numpy."""
+               return_values: bool | None = None, tie: str | None = None, sort: bool = True):
+    """Runs topk_varlen (topk_varlen_ordered with `tie`, unsorted if not
+    `sort`) on the GPU; returns (idx, vals or None, stats) as numpy."""
     x = to_device_scores(wl.x, wl.dtype, wl.width, offset)
     seq = torch.from_numpy(wl.seq_lens).cuda()
     rv = wl.return_values if return_values is None else return_values
@@ -73,7 +73,7 @@ def run_varlen(wl, use_hint: bool = True, offset: int = 0, canary: bool = True,
     if tie is None:
         idx, vals = vts.topk_varlen(x, seq, k, **kw)
     else:
-        idx, vals = vts.topk_varlen_ordered(x, seq, k, tie_break=tie, **kw)
+        idx, vals = vts.topk_varlen_ordered(x, seq, k, tie_break=tie, sort=sort, **kw)
     torch.cuda.synchronize()
     stats = vts.workspace_stats(ws)
     # self-restoring workspace: every ticket is back to zero
@@ -107,7 +107,7 @@ def check_varlen(wl, idx, vals, rows=None) -> list[str]:
 
 
 def run_transform(wl, with_raw: bool = True, ptrs: bool = True, starts: bool = True,
-                  offset: int = 0):
+                  offset: int = 0, tie: str | None = None, sort: bool = True):
     x = to_device_scores(wl.x, wl.dtype, wl.width, offset)
     L = torch.from_numpy(wl.lengths).cuda()
     rs = torch.from_numpy(wl.row_starts).cuda() if starts else None
@@ -121,7 +121,7 @@ def run_transform(wl, with_raw: bool = True, ptrs: bool = True, starts: bool = T
     out, raw = vts.topk_page_table_transform(
         x, L, pt, k, page_size=wl.page_size, row_starts=rs, page_table_row_starts=pr,
         out=ob[pad:pad + R * k], out_raw_indices=rb[pad:pad + R * k] if with_raw else None,
-        workspace=ws)
+        workspace=ws, tie_break=tie, sort=sort)
     torch.cuda.synchronize()
     stats = vts.workspace_stats(ws)
     assert int(_ticket_region(ws, R).abs().sum()) == 0

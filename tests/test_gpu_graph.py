@@ -87,6 +87,45 @@ def test_graph_replay_varlen(name, kw):
     assert int(vts.workspace_stats(ws)[1]) == 0
 
 
+@pytest.mark.parametrize("tie", ["small", "large"])
+def test_graph_replay_ordered(tie):
+    """The deterministic mode captured once (512 rows: the length-balanced
+    placement) and replayed on three input sets: every replay equals the
+    ordered oracle position by position."""
+    wls = [workloads.make("long", seed=s, hint=False, rows=512, width=32768, variant="relu")
+           for s in SEEDS]
+    w0 = wls[0]
+    R, k, dt = w0.rows, w0.k, TORCH_DTYPE[w0.dtype]
+    raw = _raw(w0).cuda()
+    x = raw.view(dt)[:, : w0.width]
+    seq = torch.from_numpy(w0.seq_lens).cuda()
+    idx = torch.empty((R, k), dtype=torch.int32, device="cuda")
+    vals = torch.empty((R, k), dtype=dt, device="cuda")
+    ws = vts.make_workspace(R, w0.width, k, dt, "cuda")
+    torch.cuda.synchronize()
+
+    def call():
+        vts.topk_varlen_ordered(x, seq, k, tie_break=tie, return_values=True, out_indices=idx,
+                                out_values=vals, workspace=ws)
+
+    say(f"graph capture ordered {tie} {tuple(x.shape)}")
+    g = _capture(call)
+    for rep, wl in enumerate(wls + wls[:1]):
+        raw.copy_(_raw(wl))
+        seq.copy_(torch.from_numpy(wl.seq_lens))
+        idx.fill_(-7)
+        vals.view(RAW_TORCH[wl.dtype]).fill_(0x5A5A)
+        torch.cuda.synchronize()
+        say(f"graph replay {rep} ordered {tie}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref_idx, ref_vals, _ = oracle.topk_varlen_ordered(wl.x[:, :wl.width], wl.dtype,
+                                                          wl.seq_lens, k, tie, return_values=True)
+        assert np.array_equal(idx.cpu().numpy(), ref_idx), f"replay {rep}: indices differ"
+        v = vals.view(RAW_TORCH[wl.dtype]).cpu().numpy().view(np.uint32)
+        assert np.array_equal(v, ref_vals), f"replay {rep}: values differ"
+
+
 def test_graph_replay_page_transform():
     wls = [workloads.make("page", seed=s, rows=16) for s in SEEDS]
     w0 = wls[0]

@@ -256,17 +256,41 @@ def test_degenerate_hints():
         _assert_ok(check_varlen(wl, idx, v))
 
 
-def test_nan_rows_do_not_crash_and_stay_valid():
-    rng = np.random.default_rng(5)
+# NaN patterns per dtype: sign clear (quiet, payload, signalling), sign set
+NAN_BITS = {F32: [0x7FC00000, 0x7FC00001, 0x7F800001, 0xFFC00000, 0xFFC00001],
+            BF16: [0x7FC0, 0x7FC1, 0x7F81, 0xFFC0, 0xFFC1],
+            F16: [0x7E00, 0x7E01, 0x7C01, 0xFE00, 0xFE01]}
+
+
+def nan_rows(dtype, W, k, rng):
+    """Rows with NaNs of both signs: sparse, everywhere, a single one, and as
+    many sign-clear NaNs as straddle the k-th place."""
+    vals = rng.standard_normal((5, W)).astype(np.float32)
+    bits = vals.view(np.uint32) if dtype == F32 else (to_bf16_bits(vals) if dtype == BF16
+                                                       else to_f16_bits(vals))
+    bits = bits.copy()
+    pat = np.array(NAN_BITS[dtype], bits.dtype)
+    bits[0, ::7] = rng.choice(pat, size=bits[0, ::7].shape)
+    bits[1, :] = rng.choice(pat, size=W)
+    bits[2, 100] = pat[3]
+    cols = rng.choice(W, size=k + 40, replace=False)
+    bits[3, cols] = rng.choice(pat[:3], size=cols.size)  # more sign-clear NaNs than k
+    cols = rng.choice(W, size=3 * k, replace=False)
+    bits[4, cols] = pat[3]  # sign-set NaNs: below everything
+    return bits
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, F16])
+def test_nan_rows(dtype):
+    """NaN rows under the order the oracle documents: the count of NaNs of
+    each sign selected and the multiset of the other values must match."""
+    rng = np.random.default_rng(5 + dtype)
     W, k = 9000, 256
-    vals = rng.standard_normal((3, W)).astype(np.float32)
-    vals[0, ::7] = np.nan
-    vals[1, :] = np.nan
-    vals[2, 100] = -np.nan
-    wl = _varlen_wl(vals, [W, W, 5000], k)
-    say("NaN rows")
+    bits = nan_rows(dtype, W, k, rng)
+    wl = _varlen_wl(None, [W, W, 5000, W, W], k, dtype=dtype, raw_bits=bits)
+    say(f"NaN rows dtype={dtype}")
     idx, v, _ = run_varlen(wl)
-    _assert_ok(check_varlen(wl, idx, v))  # NaN rows: index validity only
+    _assert_ok(check_varlen(wl, idx, v))
 
 
 def test_repeat_calls_reuse_the_workspace():

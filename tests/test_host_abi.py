@@ -182,3 +182,29 @@ def test_valid_call_without_a_gpu_reports_hip_error(lib):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present; fake pointers must not reach a launch")
     assert _varlen(lib) == HIP
+
+
+@pytest.mark.parametrize("tie", [0, 3, 4, 8, 5 | 8, -1])
+def test_ordered_entry_points_reject_bad_tie_breaks(lib, tie):
+    v = lib.vts_topk_varlen_ordered(A, 0, 8, 4096, 4096, A, 512, 1, 1, None, A, None, A, 1 << 40,
+                                    None, tie)
+    p = lib.vts_topk_page_table_transform_ordered(A, 2, 4, 1024, 1040, A, None, A, 32, 32, None,
+                                                  64, 256, A, None, A, 1 << 40, None, tie)
+    r = lib.vts_topk_transform_ragged_ordered(A, 2, 4, 1024, 1040, A, None, A, 256, A, None, A,
+                                              1 << 40, None, tie)
+    q = lib.vts_topk_transform_page1_ordered(A, 2, 4, 1024, 1040, A, None, A, 32, 32, A, 2, 256,
+                                             A, None, A, 1 << 40, None, tie)
+    assert v == p == r == q == INVALID
+
+
+@pytest.mark.parametrize("tie", [1, 2, 1 | 4, 2 | 4])
+def test_ordered_entry_points_accept_tie_breaks(lib, tie):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; fake pointers must not reach a launch")
+    # every host check passes; the call then stops at the device query
+    v = lib.vts_topk_varlen_ordered(A, 0, 8, 4096, 4096, A, 512, 1, 1, None, A, None, A, 1 << 40,
+                                    None, tie)
+    p = lib.vts_topk_page_table_transform_ordered(A, 2, 4, 1024, 1040, A, None, A, 32, 32, None,
+                                                  64, 256, A, None, A, 1 << 40, None, tie)
+    assert v == p == HIP

@@ -104,6 +104,63 @@ def test_brute_force_tiny_rows(n):
             assert np.all(sel[:-1] >= sel[1:])
 
 
+# NaN bit patterns of both signs (quiet, with a payload, signalling)
+_NAN_BITS = np.array([0x7FC00000, 0x7FC00001, 0x7F800001, 0xFFC00000, 0xFFFFFFFF], np.uint32)
+
+
+def _rank(bits32):
+    """The order the oracle documents for fp32 bits: (NaN class, value) with
+    a NaN whose sign bit is clear above +inf and one whose sign bit is set
+    below -inf (NaNs of one sign tie), numbers by value, -0 == +0."""
+    with np.errstate(invalid="ignore"):
+        v = bits32.view(np.float32).astype(np.float64)
+    nan = np.isnan(v)
+    cls = np.where(nan, np.where(bits32 >> 31 == 1, -1, 1), 0)
+    return [(int(c), 0.0 if m else float(x) + 0.0) for c, m, x in zip(cls, nan, v)]
+
+
+def _valid_subsets_ranked(rank, k):
+    n = len(rank)
+    out = []
+    for S in itertools.combinations(range(n), k):
+        rest = [j for j in range(n) if j not in S]
+        if not rest or min(rank[j] for j in S) >= max(rank[j] for j in rest):
+            out.append(S)
+    return out
+
+
+@pytest.mark.parametrize("n", [3, 5, 8])
+def test_brute_force_rows_with_nan(n):
+    """NaN order (reading: a sign-clear NaN above +inf, a sign-set one below
+    -inf, ties within a sign): the oracle's selection is a valid top-k subset
+    under that order, and every valid subset has the same count of NaNs of
+    each sign and the same multiset of the other values."""
+    rng = np.random.default_rng(300 + n)
+    pool = np.concatenate([_SMALL_VALUES.view(np.uint32), _NAN_BITS])
+    for trial in range(40):
+        bits = rng.choice(pool, size=n).astype(np.uint32)
+        rank = _rank(bits)
+        for k in range(1, n):
+            idx, _ = oracle.select(bits[None, :], F32, np.array([0]), np.array([n]), k)
+            S = tuple(sorted(idx[0].tolist()))
+            valid = _valid_subsets_ranked(rank, k)
+            assert S in valid, (bits, k, idx)
+            ref = sorted(rank[j] for j in S)
+            for V in valid:
+                assert sorted(rank[j] for j in V) == ref
+            # listed in descending order of the documented rank
+            got = [rank[j] for j in idx[0]]
+            assert all(a >= b for a, b in zip(got, got[1:]))
+
+
+def test_nan_sign_classes_by_hand():
+    # +NaN (payloads 0 and 1) above +inf, -NaN below -inf; ties by column
+    bits = np.array([0x3F800000, 0xFFC00000, 0x7F800000, 0x7FC00001, 0xFF800000, 0x7FC00000],
+                    np.uint32)  # 1, -NaN, +inf, +NaN, -inf, +NaN
+    idx, _ = oracle.select(bits[None, :], F32, np.array([0]), np.array([6]), 5)
+    assert idx[0].tolist() == [3, 5, 2, 0, 4]
+
+
 def test_brute_force_bf16_and_f16():
     rng = np.random.default_rng(7)
     for dtype, npdt in ((BF16, None), (F16, np.float16)):
@@ -425,6 +482,26 @@ def test_checker_rejects(mistake):
     assert check_rows(x, F32, base, n, k, g, idx, gv) != []
 
 
+def test_checker_on_nan_rows():
+    """Rows holding NaN: a NaN of one sign may stand for another NaN of that
+    sign (and its payload may differ), but trading a sign-clear NaN for a
+    sign-set one, or for +inf, is a different selection."""
+    bits = np.array([[0x7FC00000, 0x3F800000, 0xFFC00000, 0x7F800000, 0x7FC00001, 0xFF800000,
+                      0x40000000, 0xFFC00001]], np.uint32)  # +NaN 1 -NaN +inf +NaN' -inf 2 -NaN'
+    n, k, base = np.array([8]), 3, np.zeros(1, np.int64)
+    idx, _ = oracle.select(bits, F32, base, n, k)
+    assert sorted(idx[0].tolist()) == [0, 3, 4]  # both sign-clear NaNs, then +inf
+    assert check_rows(bits, F32, base, n, k, idx, idx) == []
+    assert check_rows(bits, F32, base, n, k, np.array([[4, 3, 0]]), idx) == []  # order free
+    for bad in ([0, 3, 2], [0, 3, 6], [0, 4, 6]):  # -NaN, 2 in place of a +NaN / +inf
+        assert check_rows(bits, F32, base, n, k, np.array([bad]), idx) != [], bad
+    # the lowest ones: -inf ranks above both sign-set NaNs
+    idx7, _ = oracle.select(bits, F32, base, n, 7)
+    assert sorted(set(range(8)) - set(idx7[0].tolist())) in ([2], [7])
+    assert check_rows(bits, F32, base, n, 7, np.array([[0, 1, 3, 4, 5, 6, 7]]), idx7) == []
+    assert check_rows(bits, F32, base, n, 7, np.array([[0, 1, 3, 4, 2, 6, 7]]), idx7) != []
+
+
 def test_transform_checker_rejects_bad_translation():
     rng = np.random.default_rng(12)
     R, W, k, ps, P = 2, 1000, 16, 64, 20
@@ -458,8 +535,8 @@ def test_ordered_hand_table(case):
     idx, v, _ = oracle.topk_varlen_ordered(x, F32, np.array([len(vals)], np.int32), k, tie,
                                            return_values=True)
     assert idx[0].tolist() == want
-    got = [vals[j] for j in want if j >= 0]
-    assert v[0][:len(got)].view(np.float32).tolist() == got
+    sel = [j for j in want if j >= 0]
+    assert v[0][:len(sel)].tolist() == x[0][sel].tolist()  # bit copies (signs of zeros kept)
 
 
 @pytest.mark.parametrize("tie", ["small", "large"])
@@ -470,25 +547,27 @@ def test_ordered_brute_force_subsets(tie):
     tied columns they hold).  The output lists it by value descending, then
     column ascending."""
     rng = np.random.default_rng(5 if tie == "small" else 6)
-    for _ in range(150):
+    # small integers, both signed zeros and NaNs of both signs: ties everywhere
+    pool = np.concatenate([np.array([-2.0, -1.0, -0.0, 0.0, 0.0, 1.0, 2.0, -0.0],
+                                    np.float32).view(np.uint32), _NAN_BITS[[0, 1, 3]]])
+    for _ in range(300):
         n = int(rng.integers(1, 8))
         k = int(rng.integers(1, 8))
-        vals = rng.integers(-2, 3, size=n).astype(np.float32)
-        vals[vals == 0] = 0.5  # no zeros: the ordered mode orders -0 below +0
-        x = vals.view(np.uint32)[None, :]
-        idx, _, _ = oracle.topk_varlen_ordered(x, F32, np.array([n], np.int32), k, tie)
+        bits = rng.choice(pool, size=n).astype(np.uint32)
+        rank = _rank(bits)
+        x = bits[None, :]
+        idx, v, _ = oracle.topk_varlen_ordered(x, F32, np.array([n], np.int32), k, tie,
+                                               return_values=True)
         m = min(n, k)
         best = None
-        for sub in itertools.combinations(range(n), m):
-            rest = [j for j in range(n) if j not in sub]
-            if rest and min(vals[list(sub)]) < max(vals[rest]):
-                continue
+        for sub in _valid_subsets_ranked(rank, m):
             key = sum(sub) if tie == "small" else -sum(sub)
             if best is None or key < best[0]:
                 best = (key, sub)
         chosen = sorted(best[1])
         got = [j for j in idx[0].tolist() if j >= 0]
-        assert sorted(got) == chosen, (vals, k, got, chosen)
+        assert sorted(got) == chosen, (bits, k, got, chosen)
         assert idx[0].tolist()[m:] == [-1] * (k - m)
         for a, b in zip(got, got[1:]):
-            assert vals[a] > vals[b] or (vals[a] == vals[b] and a < b), (vals, got)
+            assert rank[a] > rank[b] or (rank[a] == rank[b] and a < b), (bits, got)
+        assert np.array_equal(v[0][:m], bits[got])  # values: the elements' own bits

@@ -10,6 +10,10 @@ library is missing or the device is not gfx950, the calls raise.
     topk_transform_ragged(scores, lengths, offsets, top_k, ...)   -> (out, out_raw | None)
     topk_transform_page1(scores, lengths, table, cu_seqlens_q, top_k, ...) -> (out, out_raw | None)
 
+Each has a deterministic mode (``tie_break="small"`` or ``"large"``; the
+``topk_varlen_ordered`` entry point, or the ``tie_break`` argument of the
+transforms): a unique selection, in canonical order unless ``sort=False``.
+
 The C entry points, their argument contracts and the page citations are in
 ``include/vts.h``.
 """
@@ -70,6 +74,11 @@ def library():
     lib.vts_topk_page_table_transform.restype = ctypes.c_int
     lib.vts_topk_page_table_transform.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i64, i64, vp,
                                                   i32, i32, vp, vp, vp, sz, vp]
+    for name in ("vts_topk_page_table_transform", "vts_topk_transform_ragged",
+                 "vts_topk_transform_page1"):
+        f = getattr(lib, name + "_ordered")
+        f.restype = ctypes.c_int
+        f.argtypes = getattr(lib, name).argtypes + [i32]
     for name in ("vts_topk_varlen_workspace_bytes", "vts_page_transform_workspace_bytes"):
         f = getattr(lib, name)
         f.restype = sz
@@ -133,6 +142,13 @@ def _default_workspace(need: int, device, stream_ptr: int) -> torch.Tensor:
     return ws
 
 
+def _call(name: str, args: tuple, tie) -> int:
+    """Calls the C entry point `name` (its *_ordered variant with a tie code)."""
+    if tie is None:
+        return _check(name, getattr(library(), name)(*args))
+    return _check(name + "_ordered", getattr(library(), name + "_ordered")(*args, tie))
+
+
 def _check_scores(x: torch.Tensor, name: str):
     if not isinstance(x, torch.Tensor) or x.dim() != 2:
         raise ValueError(f"{name} must be a 2-D tensor")
@@ -173,6 +189,18 @@ def topk_varlen(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
 
 
 TIE_BREAK = {"small": 1, "large": 2}
+TIE_UNSORTED = 4
+
+
+def _tie_code(tie_break, sort: bool):
+    """C tie_break argument of the deterministic mode (None: unordered)."""
+    if tie_break is None:
+        if not sort:
+            raise ValueError("sort=False needs a tie_break")
+        return None
+    if tie_break not in TIE_BREAK:
+        raise ValueError(f"tie_break must be one of {sorted(TIE_BREAK)}")
+    return TIE_BREAK[tie_break] | (0 if sort else TIE_UNSORTED)
 
 
 def topk_varlen_ordered(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
@@ -180,14 +208,13 @@ def topk_varlen_ordered(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int
                         compress_ratio: int = 1, next_n: int = 1, return_values: bool = False,
                         out_indices: torch.Tensor | None = None,
                         out_values: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None, stream=None):
+                        workspace: torch.Tensor | None = None, stream=None, sort: bool = True):
     """topk_varlen in canonical order (value descending, column ascending) with
     the ties at the k-th value taken at the smallest or largest columns (see
-    vts_topk_varlen_ordered in include/vts.h)."""
-    if tie_break not in TIE_BREAK:
-        raise ValueError(f"tie_break must be one of {sorted(TIE_BREAK)}")
+    vts_topk_varlen_ordered in include/vts.h); sort=False: the same set in no
+    particular order."""
     return _varlen(logits, seq_lens, top_k, pre_idx, compress_ratio, next_n, return_values,
-                   out_indices, out_values, workspace, stream, TIE_BREAK[tie_break])
+                   out_indices, out_values, workspace, stream, _tie_code(tie_break, sort))
 
 
 def _varlen(logits, seq_lens, top_k, pre_idx, compress_ratio, next_n, return_values, out_indices,
@@ -229,8 +256,10 @@ def topk_page_table_transform(scores: torch.Tensor, lengths: torch.Tensor,
                               out: torch.Tensor | None = None,
                               out_raw_indices: torch.Tensor | None = None,
                               return_raw: bool = False, workspace: torch.Tensor | None = None,
-                              stream=None):
-    """Top-k over row windows fused with the page-table transform (include/vts.h)."""
+                              stream=None, tie_break: str | None = None, sort: bool = True):
+    """Top-k over row windows fused with the page-table transform (include/vts.h);
+    with tie_break, in the deterministic mode."""
+    tie = _tie_code(tie_break, sort)
     _check_scores(scores, "scores")
     R, W = scores.shape
     dev = scores.device
@@ -249,12 +278,11 @@ def topk_page_table_transform(scores: torch.Tensor, lengths: torch.Tensor,
     sp = _stream_ptr(stream, dev)
     if workspace is None:
         workspace = _default_workspace(workspace_bytes(R, W, top_k, scores.dtype, True), dev, sp)
-    st = library().vts_topk_page_table_transform(
-        scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
-        lengths.data_ptr(), _ptr(row_starts), pt.data_ptr(), pt.stride(0), pt.shape[1],
-        _ptr(page_table_row_starts), page_size, top_k, o.data_ptr(), _ptr(raw),
-        workspace.data_ptr(), workspace.numel(), sp)
-    _check("vts_topk_page_table_transform", st)
+    args = (scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
+            lengths.data_ptr(), _ptr(row_starts), pt.data_ptr(), pt.stride(0), pt.shape[1],
+            _ptr(page_table_row_starts), page_size, top_k, o.data_ptr(), _ptr(raw),
+            workspace.data_ptr(), workspace.numel(), sp)
+    _call("vts_topk_page_table_transform", args, tie)
     return o, raw
 
 
@@ -262,8 +290,11 @@ def topk_transform_ragged(scores: torch.Tensor, lengths: torch.Tensor,
                           topk_indices_offset: torch.Tensor, top_k: int,
                           row_starts: torch.Tensor | None = None, out: torch.Tensor | None = None,
                           out_raw_indices: torch.Tensor | None = None, return_raw: bool = False,
-                          workspace: torch.Tensor | None = None, stream=None):
-    """Top-k over row windows, each index offset into a ragged KV buffer (include/vts.h)."""
+                          workspace: torch.Tensor | None = None, stream=None,
+                          tie_break: str | None = None, sort: bool = True):
+    """Top-k over row windows, each index offset into a ragged KV buffer (include/vts.h);
+    with tie_break, in the deterministic mode."""
+    tie = _tie_code(tie_break, sort)
     _check_scores(scores, "scores")
     R, W = scores.shape
     dev = scores.device
@@ -278,11 +309,10 @@ def topk_transform_ragged(scores: torch.Tensor, lengths: torch.Tensor,
     sp = _stream_ptr(stream, dev)
     if workspace is None:
         workspace = _default_workspace(workspace_bytes(R, W, top_k, scores.dtype, True), dev, sp)
-    st = library().vts_topk_transform_ragged(
-        scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
-        lengths.data_ptr(), _ptr(row_starts), offsets.data_ptr(), top_k, o.data_ptr(), _ptr(raw),
-        workspace.data_ptr(), workspace.numel(), sp)
-    _check("vts_topk_transform_ragged", st)
+    args = (scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
+            lengths.data_ptr(), _ptr(row_starts), offsets.data_ptr(), top_k, o.data_ptr(),
+            _ptr(raw), workspace.data_ptr(), workspace.numel(), sp)
+    _call("vts_topk_transform_ragged", args, tie)
     return o, raw
 
 
@@ -290,9 +320,12 @@ def topk_transform_page1(scores: torch.Tensor, lengths: torch.Tensor, page_table
                          cu_seqlens_q: torch.Tensor, top_k: int,
                          row_starts: torch.Tensor | None = None, out: torch.Tensor | None = None,
                          out_raw_indices: torch.Tensor | None = None, return_raw: bool = False,
-                         workspace: torch.Tensor | None = None, stream=None):
+                         workspace: torch.Tensor | None = None, stream=None,
+                         tie_break: str | None = None, sort: bool = True):
     """Top-k over row windows with the page-size-1, per-request page-table
-    transform (include/vts.h, vts_topk_transform_page1)."""
+    transform (include/vts.h, vts_topk_transform_page1); with tie_break, in
+    the deterministic mode."""
+    tie = _tie_code(tie_break, sort)
     _check_scores(scores, "scores")
     R, W = scores.shape
     dev = scores.device
@@ -311,12 +344,11 @@ def topk_transform_page1(scores: torch.Tensor, lengths: torch.Tensor, page_table
     sp = _stream_ptr(stream, dev)
     if workspace is None:
         workspace = _default_workspace(workspace_bytes(R, W, top_k, scores.dtype, True), dev, sp)
-    st = library().vts_topk_transform_page1(
-        scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
-        lengths.data_ptr(), _ptr(row_starts), pt.data_ptr(), pt.stride(0), pt.shape[1],
-        cu.data_ptr(), B, top_k, o.data_ptr(), _ptr(raw), workspace.data_ptr(), workspace.numel(),
-        sp)
-    _check("vts_topk_transform_page1", st)
+    args = (scores.data_ptr(), _DTYPE[scores.dtype], R, W, scores.stride(0) if R > 1 else W,
+            lengths.data_ptr(), _ptr(row_starts), pt.data_ptr(), pt.stride(0), pt.shape[1],
+            cu.data_ptr(), B, top_k, o.data_ptr(), _ptr(raw), workspace.data_ptr(),
+            workspace.numel(), sp)
+    _call("vts_topk_transform_page1", args, tie)
     return o, raw
 
 

@@ -7,13 +7,16 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvts.so")
-SOURCES = ["vts_kernels.hip", "vts_api.hip"]
+# compiled separately and in parallel, linked in this order (the first two are
+# the kernels' code objects: any-order kernels, then the deterministic mode)
+SOURCES = ["vts_kernels.hip", "vts_kernels_ordered.hip", "vts_api.hip"]
 PROBE_LIB = os.path.join(HERE, "libvts_probe.so")
 PROBE_SOURCES = ["vts_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
+OBJDIR = os.path.join(HERE, "_build")
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # no packed-fp32 instructions in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
@@ -44,16 +47,32 @@ def _check_resources(remarks: str, out: str) -> None:
 
 
 def _compile(sources, out, verbose):
-    srcs = [os.path.join(CSRC, s) for s in sources]
+    """Compiles each source to an object (all at once), checks the kernels'
+    resource remarks, and links the objects into the shared library `out`."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = []
+    for src in sources:
+        obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+        cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
+               os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        jobs.append((cmd, obj, subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True)))
+    failed = None
+    for cmd, obj, proc in jobs:
+        _, err = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(err)
+            failed = failed or subprocess.CalledProcessError(proc.returncode, cmd)
+            continue
+        _check_resources(err, out)
+    if failed:
+        raise failed
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-Rpass-analysis=kernel-resource-usage", *srcs, "-o", tmp]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for _, o, _ in jobs], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stderr=subprocess.PIPE, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stderr)
-        raise subprocess.CalledProcessError(res.returncode, cmd)
-    _check_resources(res.stderr, out)
+    subprocess.run(cmd, check=True)
     os.replace(tmp, out)
 
 

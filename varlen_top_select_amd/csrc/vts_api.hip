@@ -127,6 +127,15 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
     p.ws_idx = reinterpret_cast<uint32_t*>(w + L.idx);
 }
 
+// tie_break argument -> internal order (false: invalid)
+bool order_of(int32_t tie_break, int32_t* order) {
+    const int32_t tb = tie_break & ~VTS_TIE_UNSORTED;
+    if (tb != VTS_TIE_SMALL && tb != VTS_TIE_LARGE) return false;
+    *order = (tb == VTS_TIE_SMALL ? ORDER_SMALL : ORDER_LARGE) |
+             ((tie_break & VTS_TIE_UNSORTED) ? ORDER_NOSORT : 0);
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -204,20 +213,21 @@ int vts_topk_varlen_ordered(const void* logits, int32_t dtype, int64_t num_rows,
                             int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
                             int32_t* out_indices, void* out_values, void* workspace,
                             size_t workspace_bytes_, void* stream, int32_t tie_break) {
-    if (tie_break != VTS_TIE_SMALL && tie_break != VTS_TIE_LARGE) return VTS_ERR_INVALID;
+    int32_t order;
+    if (!order_of(tie_break, &order)) return VTS_ERR_INVALID;
     return topk_varlen_impl(logits, dtype, num_rows, width, row_stride, seq_lens, top_k, next_n,
                             compress_ratio, pre_idx, out_indices, out_values, workspace,
-                            workspace_bytes_, stream,
-                            tie_break == VTS_TIE_SMALL ? ORDER_SMALL : ORDER_LARGE);
+                            workspace_bytes_, stream, order);
 }
 
-int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows,
-                                  int64_t width, int64_t row_stride, const int32_t* lengths,
-                                  const int32_t* row_starts, const int32_t* src_page_table,
-                                  int64_t page_table_stride, int64_t page_table_width,
-                                  const int32_t* page_table_row_starts, int32_t page_size,
-                                  int32_t top_k, int32_t* out, int32_t* out_raw_indices,
-                                  void* workspace, size_t workspace_bytes_, void* stream) {
+static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_rows,
+                               int64_t width, int64_t row_stride, const int32_t* lengths,
+                               const int32_t* row_starts, const int32_t* src_page_table,
+                               int64_t page_table_stride, int64_t page_table_width,
+                               const int32_t* page_table_row_starts, int32_t page_size,
+                               int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                               void* workspace, size_t workspace_bytes_, void* stream,
+                               int32_t order) {
     int st = check_rows(scores, dtype, num_rows, width, row_stride, top_k);
     if (st != VTS_OK) return st;
     if (page_size < 1 || page_size > (1 << 30)) return VTS_ERR_INVALID;
@@ -254,6 +264,7 @@ int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num
     p.page_size = page_size;
     p.out_idx = out;
     p.out_raw = out_raw_indices;
+    p.order = order;
     fill_plan(p, num_rows, width, workspace);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
@@ -282,11 +293,11 @@ int topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_row
                                          out, out_raw_indices, workspace, workspace_bytes_, stream);
 }
 
-int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
-                              int64_t row_stride, const int32_t* lengths,
-                              const int32_t* row_starts, const int32_t* topk_indices_offset,
-                              int32_t top_k, int32_t* out, int32_t* out_raw_indices,
-                              void* workspace, size_t workspace_bytes_, void* stream) {
+static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                       int64_t row_stride, const int32_t* lengths, const int32_t* row_starts,
+                       const int32_t* topk_indices_offset, int32_t top_k, int32_t* out,
+                       int32_t* out_raw_indices, void* workspace, size_t workspace_bytes_,
+                       void* stream, int32_t order) {
     int st = check_rows(scores, dtype, num_rows, width, row_stride, top_k);
     if (st != VTS_OK) return st;
     if (num_rows == 0) return VTS_OK;
@@ -315,19 +326,19 @@ int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_row
     p.page_size = 1;
     p.out_idx = out;
     p.out_raw = out_raw_indices;
+    p.order = order;
     fill_plan(p, num_rows, width, workspace);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
 }
 
-int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
-                             int64_t row_stride, const int32_t* lengths, const int32_t* row_starts,
-                             const int32_t* page_table, int64_t page_table_stride,
-                             int64_t page_table_width, const int32_t* cu_seqlens_q,
-                             int64_t num_batches, int32_t top_k, int32_t* out,
-                             int32_t* out_raw_indices, void* workspace, size_t workspace_bytes_,
-                             void* stream) {
+static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                      int64_t row_stride, const int32_t* lengths, const int32_t* row_starts,
+                      const int32_t* page_table, int64_t page_table_stride,
+                      int64_t page_table_width, const int32_t* cu_seqlens_q, int64_t num_batches,
+                      int32_t top_k, int32_t* out, int32_t* out_raw_indices, void* workspace,
+                      size_t workspace_bytes_, void* stream, int32_t order) {
     int st = check_rows(scores, dtype, num_rows, width, row_stride, top_k);
     if (st != VTS_OK) return st;
     if (num_batches < 0 || num_batches > INT32_MAX - 1) return VTS_ERR_INVALID;
@@ -361,6 +372,7 @@ int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows
     p.page_size = 1;
     p.out_idx = out;
     p.out_raw = out_raw_indices;
+    p.order = order;
     fill_plan(p, num_rows, width, workspace);
     const WsLayout L = ws_layout(num_rows, p.nsplit);
     int32_t* row_batch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.batch);
@@ -371,6 +383,83 @@ int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows
         return VTS_ERR_HIP;
     if (launch_transform(dtype, p, s) != hipSuccess) return VTS_ERR_HIP;
     return VTS_OK;
+}
+
+int vts_topk_page_table_transform(const void* scores, int32_t dtype, int64_t num_rows,
+                                  int64_t width, int64_t row_stride, const int32_t* lengths,
+                                  const int32_t* row_starts, const int32_t* src_page_table,
+                                  int64_t page_table_stride, int64_t page_table_width,
+                                  const int32_t* page_table_row_starts, int32_t page_size,
+                                  int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                                  void* workspace, size_t workspace_bytes_, void* stream) {
+    return page_transform_impl(scores, dtype, num_rows, width, row_stride, lengths, row_starts,
+                               src_page_table, page_table_stride, page_table_width,
+                               page_table_row_starts, page_size, top_k, out, out_raw_indices,
+                               workspace, workspace_bytes_, stream, ORDER_ANY);
+}
+
+int vts_topk_page_table_transform_ordered(
+    const void* scores, int32_t dtype, int64_t num_rows, int64_t width, int64_t row_stride,
+    const int32_t* lengths, const int32_t* row_starts, const int32_t* src_page_table,
+    int64_t page_table_stride, int64_t page_table_width, const int32_t* page_table_row_starts,
+    int32_t page_size, int32_t top_k, int32_t* out, int32_t* out_raw_indices, void* workspace,
+    size_t workspace_bytes_, void* stream, int32_t tie_break) {
+    int32_t order;
+    if (!order_of(tie_break, &order)) return VTS_ERR_INVALID;
+    return page_transform_impl(scores, dtype, num_rows, width, row_stride, lengths, row_starts,
+                               src_page_table, page_table_stride, page_table_width,
+                               page_table_row_starts, page_size, top_k, out, out_raw_indices,
+                               workspace, workspace_bytes_, stream, order);
+}
+
+int vts_topk_transform_ragged(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                              int64_t row_stride, const int32_t* lengths,
+                              const int32_t* row_starts, const int32_t* topk_indices_offset,
+                              int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                              void* workspace, size_t workspace_bytes_, void* stream) {
+    return ragged_impl(scores, dtype, num_rows, width, row_stride, lengths, row_starts,
+                       topk_indices_offset, top_k, out, out_raw_indices, workspace,
+                       workspace_bytes_, stream, ORDER_ANY);
+}
+
+int vts_topk_transform_ragged_ordered(const void* scores, int32_t dtype, int64_t num_rows,
+                                      int64_t width, int64_t row_stride, const int32_t* lengths,
+                                      const int32_t* row_starts,
+                                      const int32_t* topk_indices_offset, int32_t top_k,
+                                      int32_t* out, int32_t* out_raw_indices, void* workspace,
+                                      size_t workspace_bytes_, void* stream, int32_t tie_break) {
+    int32_t order;
+    if (!order_of(tie_break, &order)) return VTS_ERR_INVALID;
+    return ragged_impl(scores, dtype, num_rows, width, row_stride, lengths, row_starts,
+                       topk_indices_offset, top_k, out, out_raw_indices, workspace,
+                       workspace_bytes_, stream, order);
+}
+
+int vts_topk_transform_page1(const void* scores, int32_t dtype, int64_t num_rows, int64_t width,
+                             int64_t row_stride, const int32_t* lengths, const int32_t* row_starts,
+                             const int32_t* page_table, int64_t page_table_stride,
+                             int64_t page_table_width, const int32_t* cu_seqlens_q,
+                             int64_t num_batches, int32_t top_k, int32_t* out,
+                             int32_t* out_raw_indices, void* workspace, size_t workspace_bytes_,
+                             void* stream) {
+    return page1_impl(scores, dtype, num_rows, width, row_stride, lengths, row_starts, page_table,
+                      page_table_stride, page_table_width, cu_seqlens_q, num_batches, top_k, out,
+                      out_raw_indices, workspace, workspace_bytes_, stream, ORDER_ANY);
+}
+
+int vts_topk_transform_page1_ordered(const void* scores, int32_t dtype, int64_t num_rows,
+                                     int64_t width, int64_t row_stride, const int32_t* lengths,
+                                     const int32_t* row_starts, const int32_t* page_table,
+                                     int64_t page_table_stride, int64_t page_table_width,
+                                     const int32_t* cu_seqlens_q, int64_t num_batches,
+                                     int32_t top_k, int32_t* out, int32_t* out_raw_indices,
+                                     void* workspace, size_t workspace_bytes_, void* stream,
+                                     int32_t tie_break) {
+    int32_t order;
+    if (!order_of(tie_break, &order)) return VTS_ERR_INVALID;
+    return page1_impl(scores, dtype, num_rows, width, row_stride, lengths, row_starts, page_table,
+                      page_table_stride, page_table_width, cu_seqlens_q, num_batches, top_k, out,
+                      out_raw_indices, workspace, workspace_bytes_, stream, order);
 }
 
 const char* vts_status_string(int status) {

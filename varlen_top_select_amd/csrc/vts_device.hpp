@@ -57,12 +57,15 @@ __device__ __forceinline__ uint32_t gatomic_add(uint32_t* p, uint32_t v) {
 // registers at once (one being filtered, one in flight), and the filter keeps
 // a pass mask per step, so U is sized to stay under 128 VGPRs (4 waves/SIMD).
 template <int DT> struct Traits;
+// KEY_PINF / KEY_NINF: the keys of +inf and -inf (see to_key); keys above
+// KEY_PINF are NaNs with the sign clear, keys below KEY_NINF NaNs with it set.
 template <> struct Traits<F32> {
     using raw_t = uint32_t;
     static constexpr int BITS = 32;
     static constexpr int VE = 4;  // elements per 16-byte vector
     static constexpr int U = 6;
     static constexpr uint32_t PAD = 0xFF7FFFFFu;  // -FLT_MAX
+    static constexpr uint32_t KEY_PINF = 0xFF800000u, KEY_NINF = 0x007FFFFFu;
 };
 template <> struct Traits<BF16> {
     using raw_t = uint16_t;
@@ -70,6 +73,7 @@ template <> struct Traits<BF16> {
     static constexpr int VE = 8;
     static constexpr int U = 4;
     static constexpr uint32_t PAD = 0xFF7Fu;  // lowest finite bf16
+    static constexpr uint32_t KEY_PINF = 0xFF80u, KEY_NINF = 0x007Fu;
 };
 template <> struct Traits<F16> {
     using raw_t = uint16_t;
@@ -77,6 +81,7 @@ template <> struct Traits<F16> {
     static constexpr int VE = 8;
     static constexpr int U = 4;
     static constexpr uint32_t PAD = 0xFBFFu;  // lowest finite fp16
+    static constexpr uint32_t KEY_PINF = 0xFC00u, KEY_NINF = 0x03FFu;
 };
 
 // Sign-magnitude float bits -> unsigned key whose integer order is the float
@@ -98,6 +103,44 @@ __device__ __forceinline__ uint32_t from_key(uint32_t key) {
     } else {
         return (key & 0x8000u) ? (key & 0x7FFFu) : (~key & 0xFFFFu);
     }
+}
+
+// Keys of the deterministic mode, where elements that compare as equal values
+// must share one key: -0 takes the key of +0, every NaN with the sign clear
+// the largest key and every NaN with the sign set the smallest.  The key
+// order is then the value order (NaNs above +inf or below -inf) with every tie
+// explicit, so a column tie-break makes it total.  Keys stay in the dtype's
+// range; a canonical key no longer names its element's bits for -0 and NaN
+// (canon_special), which are read back from the row where values are output.
+template <int DT>
+__device__ __forceinline__ uint32_t canon_key(uint32_t key) {
+    constexpr uint32_t POS0 = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
+    constexpr uint32_t KMAX = Traits<DT>::BITS == 32 ? 0xFFFFFFFFu : 0xFFFFu;
+    key = key == POS0 - 1u ? POS0 : key;
+    key = key > Traits<DT>::KEY_PINF ? KMAX : key;
+    return key < Traits<DT>::KEY_NINF ? 0u : key;
+}
+
+// whether a canonical key may stand for elements of other bits (+-0, NaN)
+template <int DT>
+__device__ __forceinline__ bool canon_special(uint32_t key) {
+    constexpr uint32_t POS0 = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
+    constexpr uint32_t KMAX = Traits<DT>::BITS == 32 ? 0xFFFFFFFFu : 0xFFFFu;
+    return key == POS0 || key == KMAX || key == 0u;
+}
+
+// The largest threshold t' <= t for which "canonical key >= t'" and the
+// raw-bit test of RungTest (signed compare of the element bits with t's
+// bits, used when t has the sign bit of a key set) agree on every element:
+// +0's key becomes -0's (no canonical key equals it, and it is below +0, so
+// the raw-bit test is not used), and a threshold inside the NaN range becomes
+// the smallest NaN key (every NaN with the sign clear passes both tests).
+// Lowering a threshold only admits more candidates.
+template <int DT>
+__device__ __forceinline__ uint32_t canon_floor(uint32_t t) {
+    constexpr uint32_t POS0 = Traits<DT>::BITS == 32 ? 0x80000000u : 0x8000u;
+    t = t > Traits<DT>::KEY_PINF + 1u ? Traits<DT>::KEY_PINF + 1u : t;
+    return t == POS0 ? POS0 - 1u : t;
 }
 
 __device__ __forceinline__ uint32_t lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
@@ -348,6 +391,9 @@ __device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, 
     if (((lo ^ hi) & ~low_mask) == 0) {  // all keys share the bits that matter
         kth = lo & ~low_mask;
         n_greater = 0;
+        // (uniform branch) the barrier that a pass would end with: lo and hi
+        // came from block_minmax, whose per-wave slots the next one rewrites
+        lds_sync();
         return;
     }
     const int hb = 31 - __clz(lo ^ hi);

@@ -22,9 +22,11 @@ constexpr int BALANCE_XCDS = 8;
 constexpr int BALANCE_CUS_PER_XCD = 32;
 constexpr int BALANCE_CUS = BALANCE_XCDS * BALANCE_CUS_PER_XCD;
 
-// Output order: any (fastest), or canonical (value descending, column
-// ascending) with the boundary ties taken at the smallest or largest columns.
-constexpr int ORDER_ANY = 0, ORDER_SMALL = 1, ORDER_LARGE = 2;
+// Output order: any (fastest), or the deterministic mode: the ties at the
+// k-th value taken at the smallest (ORDER_SMALL) or largest (ORDER_LARGE)
+// columns, listed in canonical order (value descending, column ascending)
+// unless ORDER_NOSORT is added (the same set, in no particular order).
+constexpr int ORDER_ANY = 0, ORDER_SMALL = 1, ORDER_LARGE = 2, ORDER_NOSORT = 4;
 
 struct Params {
     // score rows
@@ -70,7 +72,7 @@ struct Params {
     uint32_t* ws_count_up;  // of which keys >= the likely rung, per unit
     uint32_t* ws_key;
     uint32_t* ws_idx;
-    int32_t order;  // ORDER_ANY, or canonical order with a tie-break (ORDER_SMALL/LARGE)
+    int32_t order;  // ORDER_ANY, or ORDER_SMALL / ORDER_LARGE (+ ORDER_NOSORT)
 };
 
 enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };
@@ -98,6 +100,8 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
 
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream);
+hipError_t launch_varlen_ordered(int dtype, const Params& p, hipStream_t stream);
+hipError_t launch_transform_ordered(int dtype, const Params& p, hipStream_t stream);
 // Writes each row's request b (cu_seqlens[b] <= row < cu_seqlens[b + 1]) or -1.
 hipError_t launch_row_batch(const int32_t* cu_seqlens, int32_t num_batches, int32_t num_rows,
                             int32_t* row_batch, hipStream_t stream);
