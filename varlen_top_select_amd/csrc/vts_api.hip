@@ -82,13 +82,22 @@ int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width) {
     return VTS_OK;
 }
 
-// gfx950 check, cached per device.
-int check_device() {
+// The device that work on `stream` runs on (the current device for the null
+// stream), checked to be a gfx950, the result cached per device.
+int check_device(void* stream, int* dev_out = nullptr) {
     static std::mutex mu;
     static int known[64];  // 0 unknown, 1 gfx950, 2 other
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return VTS_ERR_HIP;
+    if (stream == nullptr) {
+        if (hipGetDevice(&dev) != hipSuccess) return VTS_ERR_HIP;
+    } else {
+        hipDevice_t d;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &d) != hipSuccess)
+            return VTS_ERR_HIP;
+        dev = (int)d;
+    }
     if (dev < 0 || dev >= 64) return VTS_ERR_UNSUPPORTED;
+    if (dev_out) *dev_out = dev;
     std::lock_guard<std::mutex> lock(mu);
     if (known[dev] == 0) {
         hipDeviceProp_t prop;
@@ -98,9 +107,12 @@ int check_device() {
     return known[dev] == 1 ? VTS_OK : VTS_ERR_UNSUPPORTED;
 }
 
-void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
+// The launch plan and the workspace pointers; `slots` candidate slots per
+// unit in the workspace (>= CAP whenever a row is split: a split row's units
+// publish their on-chip lists there).
+void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots = HI_SLOTS) {
     const int32_t ns = plan_nsplit(num_rows, width);
-    const WsLayout L = ws_layout(num_rows, ns);
+    const WsLayout L = ws_layout(num_rows, ns, slots);
     char* w = static_cast<char*>(ws);
     p.nsplit = ns;
     p.min_chunk = g_tune.min_chunk > 0 ? g_tune.min_chunk : MIN_CHUNK;
@@ -114,7 +126,9 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws) {
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
     p.hi_cap = HI_SLOTS;
     if (g_tune.spill_slots > 0) p.hi_cap = g_tune.spill_slots;
+    if (p.hi_cap > slots) p.hi_cap = slots;
     if (p.hi_cap < p.lds_cap) p.hi_cap = p.lds_cap;
+    p.ws_slots = slots;
     p.force_path = g_tune.force_path;
     p.sigma = (g_tune.sigma_tenths > 0 ? g_tune.sigma_tenths : 50) / 10.0f;
     p.sigma2 = (g_tune.likely_tenths > 0 ? g_tune.likely_tenths : 20) / 10.0f;
@@ -177,7 +191,7 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     }
     st = check_workspace(workspace, workspace_bytes_, num_rows, width);
     if (st != VTS_OK) return st;
-    st = check_device();
+    st = check_device(stream);
     if (st != VTS_OK) return st;
 
     Params p;
@@ -243,7 +257,7 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
     st = check_workspace(workspace, workspace_bytes_, num_rows, width);
     if (st != VTS_OK) return st;
-    st = check_device();
+    st = check_device(stream);
     if (st != VTS_OK) return st;
 
     Params p;
@@ -308,7 +322,7 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
     st = check_workspace(workspace, workspace_bytes_, num_rows, width);
     if (st != VTS_OK) return st;
-    st = check_device();
+    st = check_device(stream);
     if (st != VTS_OK) return st;
 
     Params p;
@@ -352,7 +366,7 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
     st = check_workspace(workspace, workspace_bytes_, num_rows, width);
     if (st != VTS_OK) return st;
-    st = check_device();
+    st = check_device(stream);
     if (st != VTS_OK) return st;
 
     Params p;

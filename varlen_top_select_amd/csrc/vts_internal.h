@@ -8,11 +8,11 @@
 
 namespace vts {
 
-// Candidate slots per workgroup in the workspace: slots [0, HI_SLOTS) mirror
-// the unit's candidate list (the first, on-chip slots are copied there only
-// when a split row publishes them; later slots are where the list spills).
+// Candidate slots per workgroup in the workspace (Params::ws_slots, at most
+// HI_SLOTS): they mirror the unit's candidate list (the first, on-chip slots
+// are copied there only when a split row publishes them; later slots are
+// where the list spills).
 constexpr int HI_SLOTS = 8192;
-constexpr int WSCAP = HI_SLOTS;
 
 // Compute units of an MI355X: 8 XCDs of 32.  Block b of a launch goes to XCD
 // b % 8, and there the k-th block (b = 8k + x) to compute unit k % 32 while
@@ -61,7 +61,8 @@ struct Params {
     int32_t units_per_xcd;
     int32_t balance;    // 1: rows are assigned to workgroups by length (see balanced_row)
     int32_t lds_cap;    // on-chip candidate slots used before spilling (<= CAP)
-    int32_t hi_cap;     // candidate slots in all (<= HI_SLOTS) before re-filtering
+    int32_t hi_cap;     // candidate slots in all (<= ws_slots) before re-filtering
+    int32_t ws_slots;   // workspace slots per unit (the stride of ws_key / ws_idx)
     int32_t force_path;
     float sigma;        // margin of the safe rung, in standard deviations
     float sigma2;       // margin of the likely rung (<= sigma)
@@ -84,7 +85,7 @@ struct WsLayout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
+inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit, int32_t slots = HI_SLOTS) {
     WsLayout L;
     const size_t units = (size_t)num_rows * (size_t)nsplit;
     L.stats = 0;
@@ -92,8 +93,8 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit) {
     L.count = L.ticket + align256((size_t)num_rows * 4);
     L.count_up = L.count + align256(units * 4);
     L.key = L.count_up + align256(units * 4);
-    L.idx = L.key + align256(units * WSCAP * 4);
-    L.batch = L.idx + align256(units * WSCAP * 4);  // one int32 per row (request map)
+    L.idx = L.key + align256(units * (size_t)slots * 4);
+    L.batch = L.idx + align256(units * (size_t)slots * 4);  // one int32 per row (request map)
     L.total = L.batch + align256((size_t)num_rows * 4);
     return L;
 }

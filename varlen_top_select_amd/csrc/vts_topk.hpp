@@ -1498,8 +1498,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     if (c >= eff) return;
 
     const Slice s = make_slice<DT>(row, n, c, eff);
-    uint32_t* gkey = p.ws_key + (size_t)unit * WSCAP;
-    uint32_t* gidx = p.ws_idx + (size_t)unit * WSCAP;
+    uint32_t* gkey = p.ws_key + (size_t)unit * (uint32_t)p.ws_slots;
+    uint32_t* gidx = p.ws_idx + (size_t)unit * (uint32_t)p.ws_slots;
     const Buf B{gkey, gidx, (uint32_t)p.lds_cap, (uint32_t)p.hi_cap};
     // body vectors of this unit, relative indexing (32-bit)
     const u32x4* vb = reinterpret_cast<const u32x4*>(row + s.h) + s.v0;
@@ -1673,8 +1673,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         return;
     }
     const bool rupper = !mixed && tup >= (uint32_t)p.k;
-    const uint32_t* rkey = p.ws_key + (size_t)unit0 * WSCAP;
-    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * WSCAP;
+    const uint32_t* rkey = p.ws_key + (size_t)unit0 * (uint32_t)p.ws_slots;
+    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * (uint32_t)p.ws_slots;
     if (threadIdx.x == 0) {
         if (th > (uint32_t)CAP) gatomic_add(p.ws_stats + 2, 1u);
         if (!rupper) gatomic_add(p.ws_stats + 3, 1u);
@@ -1707,7 +1707,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
                 if (i < m) {
                     int q = 0;  // the list holding gathered entry i
                     while (q + 1 < eff && sm.seg_lo[q + 1] <= i) ++q;
-                    const size_t at = (size_t)q * WSCAP + (i - sm.seg_lo[q]) + (q == c ? own : 0u);
+                    const size_t at = (size_t)q * (uint32_t)p.ws_slots + (i - sm.seg_lo[q]) +
+                                      (q == c ? own : 0u);
                     kk[e] = gload(rkey + at);
                     cc[e] = gload(ridx + at);
                 }
@@ -1734,8 +1735,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         const uint32_t mq = sm.seg_hi[q];
         const uint32_t from = q == c ? own : 0u;
         if (mq > from)
-            ingest_global<DT>(sm, p.k, rkey + (size_t)q * WSCAP + from,
-                              ridx + (size_t)q * WSCAP + from, mq - from, thr);
+            ingest_global<DT>(sm, p.k, rkey + (size_t)q * (uint32_t)p.ws_slots + from,
+                              ridx + (size_t)q * (uint32_t)p.ws_slots + from, mq - from, thr);
     }
     __syncthreads();
     const uint32_t m = sm.cand_n;
