@@ -54,7 +54,10 @@ typedef enum {
     /* workspace pointer null or smaller than the matching *_workspace_bytes(). */
     VTS_ERR_WORKSPACE = -3,
     /* a HIP runtime call failed (no device, launch failure). */
-    VTS_ERR_HIP = -4
+    VTS_ERR_HIP = -4,
+    /* vts_topk_varlen_noalloc: the shape needs more scratch than its fixed
+     * device array holds. */
+    VTS_ERR_TOO_LARGE = -5
 } vts_status;
 
 /* Workspace: device scratch used by rows that several workgroups share and by
@@ -115,6 +118,32 @@ int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t
                     int64_t row_stride, const int32_t* seq_lens, int32_t top_k, int32_t next_n,
                     int32_t compress_ratio, const int32_t* pre_idx, int32_t* out_indices,
                     void* out_values, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * vts_topk_varlen_noalloc -- vts_topk_varlen for callers that cannot allocate
+ * device memory (code being captured into a HIP graph, tight serving loops,
+ * harnesses that forbid allocation): the same arguments, results and errors,
+ * without the workspace.  Its scratch is a fixed 32 MiB device array of the
+ * library (one per device, held from the library's first use of that device
+ * until the process ends); the call allocates nothing and frees nothing.
+ *
+ * Limit: the shape's workspace must fit the array with at least 3776
+ * candidate slots per workgroup; otherwise VTS_ERR_TOO_LARGE and nothing is
+ * enqueued.  That admits up to about 1100 row units (rows times workgroups
+ * per row; e.g. 1024 rows of 262144 columns, or 64 rows split in four),
+ * with fewer spill slots per unit than the workspace entry point when it is
+ * near the limit (a spill beyond them takes the slower, still exact,
+ * re-filtering path).
+ *
+ * Each call first clears the array's counters and row tickets on `stream`
+ * (a small kernel), then runs the selection.  Every call on one device shares
+ * that device's array: calls that can overlap on one device (two streams, two
+ * threads) race and must be serialised by the caller.
+ */
+int vts_topk_varlen_noalloc(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                            int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
+                            int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
+                            int32_t* out_indices, void* out_values, void* stream);
 
 /* Tie-breaks of the deterministic mode (the *_ordered entry points). */
 enum vts_tie_break {

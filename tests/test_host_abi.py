@@ -208,3 +208,12 @@ def test_ordered_entry_points_accept_tie_breaks(lib, tie):
     p = lib.vts_topk_page_table_transform_ordered(A, 2, 4, 1024, 1040, A, None, A, 32, 32, None,
                                                   64, 256, A, None, A, 1 << 40, None, tie)
     assert v == p == HIP
+
+
+def test_noalloc_rejects_a_shape_beyond_its_scratch_on_the_host(lib):
+    # 2048 rows of 262144 columns: more row units than the fixed scratch holds;
+    # the check runs on the host before any device call (so also without a GPU)
+    st = lib.vts_topk_varlen_noalloc(A, 0, 2048, 262144, 262144, A, 2048, 1, 1, None, A, None,
+                                     None)
+    assert st == -5
+    assert b"scratch" in lib.vts_status_string(st)

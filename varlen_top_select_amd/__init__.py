@@ -25,7 +25,7 @@ import warnings
 
 import torch
 
-__all__ = ["topk_varlen", "topk_varlen_ordered", "topk_page_table_transform", "topk_transform_ragged",
+__all__ = ["topk_varlen", "topk_varlen_noalloc", "topk_varlen_ordered", "topk_page_table_transform", "topk_transform_ragged",
            "topk_transform_page1",
            "workspace_bytes", "make_workspace",
            "set_tuning", "workspace_stats", "VtsError", "library", "LIB_PATH"]
@@ -62,6 +62,9 @@ def library():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.vts_topk_varlen.restype = ctypes.c_int
     lib.vts_topk_varlen.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.vts_topk_varlen_noalloc.restype = ctypes.c_int
+    lib.vts_topk_varlen_noalloc.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp,
+                                            vp]
     lib.vts_topk_varlen_ordered.restype = ctypes.c_int
     lib.vts_topk_varlen_ordered.argtypes = [vp, i32, i64, i64, i64, vp, i32, i32, i32, vp, vp, vp,
                                             vp, sz, vp, i32]
@@ -186,6 +189,32 @@ def topk_varlen(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
     """Exact top-k of each row's valid prefix (see vts_topk_varlen in include/vts.h)."""
     return _varlen(logits, seq_lens, top_k, pre_idx, compress_ratio, next_n, return_values,
                    out_indices, out_values, workspace, stream, None)
+
+
+def topk_varlen_noalloc(logits: torch.Tensor, seq_lens: torch.Tensor, top_k: int,
+                        out_indices: torch.Tensor, out_values: torch.Tensor | None = None,
+                        pre_idx: torch.Tensor | None = None, compress_ratio: int = 1,
+                        next_n: int = 1, stream=None):
+    """topk_varlen without a workspace: the library's fixed device scratch
+    (vts_topk_varlen_noalloc in include/vts.h).  The caller passes the
+    outputs; nothing is allocated.  Calls that can overlap on one device race."""
+    _check_scores(logits, "logits")
+    R, W = logits.shape
+    dev = logits.device
+    if next_n < 1 or R % next_n:
+        raise ValueError("num_rows must be a multiple of next_n")
+    seq_lens = _i32(seq_lens, "seq_lens", R // next_n, dev)
+    if out_indices is None:
+        raise ValueError("out_indices is required")
+    idx = _out(out_indices, (R, top_k), torch.int32, dev, "out_indices")
+    vals = None if out_values is None else _out(out_values, (R, top_k), logits.dtype, dev,
+                                                "out_values")
+    st = library().vts_topk_varlen_noalloc(
+        logits.data_ptr(), _DTYPE[logits.dtype], R, W, logits.stride(0) if R > 1 else W,
+        seq_lens.data_ptr(), top_k, next_n, compress_ratio, _ptr(pre_idx), idx.data_ptr(),
+        _ptr(vals), _stream_ptr(stream, dev))
+    _check("vts_topk_varlen_noalloc", st)
+    return idx, vals
 
 
 TIE_BREAK = {"small": 1, "large": 2}

@@ -107,6 +107,44 @@ int check_device(void* stream, int* dev_out = nullptr) {
     return known[dev] == 1 ? VTS_OK : VTS_ERR_UNSUPPORTED;
 }
 
+// Device scratch of vts_topk_varlen_noalloc, for callers that cannot
+// allocate: one array per device, held by the loaded library until the
+// process ends.  Host code never names it except in hipGetSymbolAddress, which
+// gives each device's own address (scratch_of); those addresses are what the
+// launches take.
+constexpr size_t SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[SCRATCH_BYTES];
+
+// The address of `scratch` on device `dev`, looked up once per device with
+// that device current.
+int scratch_of(int dev, void** out) {
+    static std::mutex mu;
+    static void* addr[64];
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return VTS_ERR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return VTS_ERR_HIP;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return VTS_ERR_HIP;
+        if (e != hipSuccess || ptr == nullptr) return VTS_ERR_HIP;
+        addr[dev] = ptr;
+    }
+    *out = addr[dev];
+    return VTS_OK;
+}
+
+// Candidate slots per unit that let the workspace of this shape fit the
+// scratch array (at most HI_SLOTS, in steps of 64), or 0 when even CAP slots
+// per unit -- what a split row's units publish -- do not fit.
+int32_t scratch_slots(int64_t num_rows, int64_t width) {
+    const int32_t ns = plan_nsplit(num_rows, width);
+    for (int32_t slots = HI_SLOTS; slots >= CAP; slots -= 64)
+        if (ws_layout(num_rows, ns, slots).total <= SCRATCH_BYTES) return slots;
+    return 0;
+}
+
 // The launch plan and the workspace pointers; `slots` candidate slots per
 // unit in the workspace (>= CAP whenever a row is split: a split row's units
 // publish their on-chip lists there).
@@ -169,11 +207,14 @@ int vts_workspace_init(void* workspace, size_t bytes, void* stream) {
     return VTS_OK;
 }
 
+// use_scratch: the device's scratch array instead of the caller's workspace
+// (vts_topk_varlen_noalloc)
 static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
                             int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
                             int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
                             int32_t* out_indices, void* out_values, void* workspace,
-                            size_t workspace_bytes_, void* stream, int32_t order) {
+                            size_t workspace_bytes_, void* stream, int32_t order,
+                            bool use_scratch = false) {
     int st = check_rows(logits, dtype, num_rows, width, row_stride, top_k);
     if (st != VTS_OK) return st;
     if (next_n < 1 || compress_ratio < 1 || num_rows % next_n != 0) return VTS_ERR_INVALID;
@@ -189,10 +230,27 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
         pre_idx = nullptr;
         warn = VTS_WARN_HINT_DISCARDED;
     }
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    int32_t slots = HI_SLOTS;
+    if (use_scratch) {
+        slots = scratch_slots(num_rows, width);
+        if (slots == 0) return VTS_ERR_TOO_LARGE;
+    } else {
+        st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+        if (st != VTS_OK) return st;
+    }
+    int dev = 0;
+    st = check_device(stream, &dev);
     if (st != VTS_OK) return st;
-    st = check_device(stream);
-    if (st != VTS_OK) return st;
+    if (use_scratch) {
+        st = scratch_of(dev, &workspace);
+        if (st != VTS_OK) return st;
+        // the scratch keeps the last call's contents, which may have another
+        // layout: clear the counters and row tickets, which must start at zero
+        const WsLayout L = ws_layout(num_rows, plan_nsplit(num_rows, width), slots);
+        if (launch_zero(static_cast<uint32_t*>(workspace), L.count / 4,
+                        static_cast<hipStream_t>(stream)) != hipSuccess)
+            return VTS_ERR_HIP;
+    }
 
     Params p;
     memset(&p, 0, sizeof(p));
@@ -208,7 +266,7 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     p.out_idx = out_indices;
     p.out_vals = out_values;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace);
+    fill_plan(p, num_rows, width, workspace, slots);
     if (launch_varlen(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess) return VTS_ERR_HIP;
     return warn;
 }
@@ -220,6 +278,15 @@ int vts_topk_varlen(const void* logits, int32_t dtype, int64_t num_rows, int64_t
     return topk_varlen_impl(logits, dtype, num_rows, width, row_stride, seq_lens, top_k, next_n,
                             compress_ratio, pre_idx, out_indices, out_values, workspace,
                             workspace_bytes_, stream, ORDER_ANY);
+}
+
+int vts_topk_varlen_noalloc(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
+                            int64_t row_stride, const int32_t* seq_lens, int32_t top_k,
+                            int32_t next_n, int32_t compress_ratio, const int32_t* pre_idx,
+                            int32_t* out_indices, void* out_values, void* stream) {
+    return topk_varlen_impl(logits, dtype, num_rows, width, row_stride, seq_lens, top_k, next_n,
+                            compress_ratio, pre_idx, out_indices, out_values, nullptr, 0,
+                            stream, ORDER_ANY, true);
 }
 
 int vts_topk_varlen_ordered(const void* logits, int32_t dtype, int64_t num_rows, int64_t width,
@@ -484,6 +551,8 @@ const char* vts_status_string(int status) {
         case VTS_ERR_UNSUPPORTED: return "unsupported request or device";
         case VTS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
         case VTS_ERR_HIP: return "HIP runtime error";
+        case VTS_ERR_TOO_LARGE:
+            return "the call needs more device scratch than vts_topk_varlen_noalloc holds (32 MiB)";
     }
     return "unknown status";
 }

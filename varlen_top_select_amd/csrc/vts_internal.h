@@ -102,6 +102,8 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit, int32_t slots = HI_S
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_varlen_ordered(int dtype, const Params& p, hipStream_t stream);
+// Zeroes `words` 32-bit words at `p` (a kernel, so it can sit in a captured graph).
+hipError_t launch_zero(uint32_t* p, size_t words, hipStream_t stream);
 hipError_t launch_transform_ordered(int dtype, const Params& p, hipStream_t stream);
 // Writes each row's request b (cu_seqlens[b] <= row < cu_seqlens[b + 1]) or -1.
 hipError_t launch_row_batch(const int32_t* cu_seqlens, int32_t num_batches, int32_t num_rows,

@@ -50,6 +50,18 @@ hipError_t launch_row_batch(const int32_t* cu_seqlens, int32_t num_batches, int3
     return hipGetLastError();
 }
 
+__global__ void __launch_bounds__(NT) zero_kernel(uint32_t* p, uint32_t words) {
+    const uint32_t i = blockIdx.x * NT + threadIdx.x;
+    if (i < words) gstore(p + i, 0u);
+}
+
+hipError_t launch_zero(uint32_t* p, size_t words, hipStream_t stream) {
+    if (words == 0) return hipSuccess;
+    const uint32_t grid = (uint32_t)((words + NT - 1) / NT);
+    hipLaunchKernelGGL(zero_kernel, dim3(grid), dim3(NT), 0, stream, p, (uint32_t)words);
+    return hipGetLastError();
+}
+
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream) {
     if (p.order != ORDER_ANY) return launch_transform_ordered(dtype, p, stream);
     switch (dtype) {
