@@ -212,6 +212,21 @@ def read_ceiling(nbytes: int, torch) -> float | None:
     return nbytes / float(np.median(ts)) / 1e9
 
 
+def launch_floor(torch, reps: int = 20) -> float | None:
+    """Cold median µs of the smallest launch: one workgroup reading 16 bytes,
+    timed like the workloads (read flush, one event pair around the call)."""
+    path = os.path.join(ROOT, "varlen_top_select_amd", "libvts_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.vts_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(16, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    ts = cold_times(lambda: lib.vts_probe_read(buf.data_ptr(), 16, sink.data_ptr(), s), torch, reps)
+    return float(np.median(ts))
+
+
 def stored_traffic(src_hash: str):
     """HBM bytes per launch from the committed counter summary, if it matches this source."""
     path = os.path.join(ROOT, "profiles", "topk_long_batch_traffic.json")
@@ -401,6 +416,10 @@ def main() -> int:
                 "valid_GBps": round(vb2 / (np.median(ct2) * 1e-6) / 1e9, 1),
                 "valid_bytes": vb2}
             del s2, ws2
+        lf = launch_floor(torch)
+        if lf is not None:
+            others["launch_floor"] = {"us_median_cold": round(lf, 2),
+                                      "what": "one workgroup reading 16 bytes, same protocol"}
         line["others"] = others
 
     if not args.no_cpu:

@@ -37,6 +37,10 @@ struct Tuning {
     int32_t no_balance = 0;
 } g_tune;
 
+#ifdef VTS_PHASE_STAMPS
+uint64_t* g_stamps = nullptr;  // phase-timing build: where the next launches stamp
+#endif
+
 int32_t plan_nsplit(int64_t num_rows, int64_t width) {
     if (g_tune.nsplit > 0) return g_tune.nsplit;
     if (num_rows <= 0) return 1;
@@ -177,6 +181,9 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slo
     p.ws_count_up = reinterpret_cast<uint32_t*>(w + L.count_up);
     p.ws_key = reinterpret_cast<uint32_t*>(w + L.key);
     p.ws_idx = reinterpret_cast<uint32_t*>(w + L.idx);
+#ifdef VTS_PHASE_STAMPS
+    p.stamps = g_stamps;
+#endif
 }
 
 // tie_break argument -> internal order (false: invalid)
@@ -542,6 +549,12 @@ int vts_topk_transform_page1_ordered(const void* scores, int32_t dtype, int64_t 
                       page_table_stride, page_table_width, cu_seqlens_q, num_batches, top_k, out,
                       out_raw_indices, workspace, workspace_bytes_, stream, order);
 }
+
+#ifdef VTS_PHASE_STAMPS
+// Phase-timing build only: launches after this call write 8 stamps per unit
+// (row unit u at stamps[8u .. 8u + 7]) into `stamps` (device, or null: off).
+void vts_phase_stamps(void* stamps) { g_stamps = static_cast<uint64_t*>(stamps); }
+#endif
 
 const char* vts_status_string(int status) {
     switch (status) {

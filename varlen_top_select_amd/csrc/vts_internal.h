@@ -74,6 +74,9 @@ struct Params {
     uint32_t* ws_key;
     uint32_t* ws_idx;
     int32_t order;  // ORDER_ANY, or ORDER_SMALL / ORDER_LARGE (+ ORDER_NOSORT)
+#ifdef VTS_PHASE_STAMPS
+    uint64_t* stamps;  // phase-timing build: 8 stamps per unit, or null
+#endif
 };
 
 enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };

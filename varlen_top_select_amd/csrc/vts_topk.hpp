@@ -1446,6 +1446,38 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
 // the kernel
 // ---------------------------------------------------------------------------
 
+// Phase stamps, compiled in only for the phase-timing build (-DVTS_PHASE_STAMPS,
+// varlen_top_select_amd/phases.py): thread 0 of a unit writes the 100 MHz
+// real-time counter when the unit starts (0), knows its window (1), has its
+// rungs (2), has streamed (3), has written its outputs (4) and has taken its
+// split-row ticket (5); slot 6 holds the hardware id (HW_ID | XCC_ID << 32)
+// and slot 7 the row and its valid length.
+#ifdef VTS_PHASE_STAMPS
+#define VTS_STAMP(i)                                                           \
+    do {                                                                       \
+        if (threadIdx.x == 0 && p.stamps)                                      \
+            gstore(p.stamps + (size_t)unit * 8 + (i),                          \
+                   (uint64_t)__builtin_amdgcn_s_memrealtime());                \
+    } while (0)
+#define VTS_STAMP_ID(row, len)                                                 \
+    do {                                                                       \
+        if (threadIdx.x == 0 && p.stamps) {                                    \
+            gstore(p.stamps + (size_t)unit * 8 + 6,                            \
+                   (uint64_t)__builtin_amdgcn_s_getreg(0xF804) |               \
+                       ((uint64_t)__builtin_amdgcn_s_getreg(0xF814) << 32));   \
+            gstore(p.stamps + (size_t)unit * 8 + 7,                            \
+                   (uint64_t)(uint32_t)(row) | ((uint64_t)(len) << 32));       \
+        }                                                                      \
+    } while (0)
+#else
+#define VTS_STAMP(i) \
+    do {             \
+    } while (0)
+#define VTS_STAMP_ID(row, len) \
+    do {                       \
+    } while (0)
+#endif
+
 template <int DT, class Policy>
 __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     using raw_t = typename Traits<DT>::raw_t;
@@ -1457,6 +1489,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const uint32_t bid = blockIdx.x;
     const uint32_t unit = (bid & 7u) * (uint32_t)p.units_per_xcd + (bid >> 3);
     if (unit >= (uint32_t)p.num_units) return;
+    VTS_STAMP(0);
     // The row and its window are the same in every lane, but they arrive
     // through LDS and vector loads; readfirstlane puts them in scalar
     // registers, so the stream's buffer offsets are scalar and its loads need
@@ -1474,6 +1507,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     // window starts and lengths lie in [0, width], width < 2^31
     base = __builtin_amdgcn_readfirstlane((int)base);
     n = __builtin_amdgcn_readfirstlane((int)n);
+    VTS_STAMP(1);
+    VTS_STAMP_ID(r, n);
     const raw_t* row = static_cast<const raw_t*>(p.x) + (int64_t)r * p.row_stride + base;
     if (n <= p.k) {
         if (c == 0) {
@@ -1489,6 +1524,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
                 short_row<DT, Policy>(p, r, base, n, row);
             }
         }
+        VTS_STAMP(4);
         return;
     }
     int64_t eff64 = (n + p.min_chunk - 1) / p.min_chunk;
@@ -1551,6 +1587,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
             G.T2 = canon_floor<DT>(G.T2);
         }
     }
+    VTS_STAMP(2);
 
     uint32_t nh = 0, nup = 0;  // candidates (keys >= T), of which keys >= T2
     if (direct) {
@@ -1568,6 +1605,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         __syncthreads();  // also completes the workspace stores of every thread
         nh = sm.cand_n;
         nup = sm.up_n;
+        VTS_STAMP(3);
         hist_clear(sm);  // the staging queues overlaid the histogram
         lds_sync();      // everyone has read the counts before they can change
         if (nh > B.hi_cap) {  // slots ran out: re-filter with compaction
@@ -1594,18 +1632,21 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
             if (threadIdx.x == 0 && nh < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
             __syncthreads();
             whole_row<DT, Policy>(sm, p, r, base, n, row);
+            VTS_STAMP(4);
             return;
         }
         if (threadIdx.x == 0 && !upper && !whole_list) gatomic_add(p.ws_stats + 3, 1u);
         const uint32_t thr = upper ? G.T2 : 0u;
         if (nh <= own) {  // every candidate on chip: the usual case
             select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, nh, thr));
+            VTS_STAMP(4);
             return;
         }
         if (nh <= (uint32_t)(20 * NT)) {
             // the on-chip slots and the spilled ones, selected as they are
             if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
             select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<20>(sm, own, gkey, gidx, nh, thr));
+            VTS_STAMP(4);
             return;
         }
         // a long spill: pull it into LDS with the compaction filter
@@ -1620,6 +1661,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         const uint32_t m = sm.cand_n;
         __syncthreads();
         select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, m));
+        VTS_STAMP(4);
         return;
     }
 
@@ -1649,6 +1691,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         sm.flag = last ? 1u : 0u;
     }
     __syncthreads();
+    VTS_STAMP(5);
     if (sm.flag == 0) return;
 
     // last unit of the row: merge
@@ -1670,6 +1713,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         if (threadIdx.x == 0 && th < (uint32_t)p.k) gatomic_add(p.ws_stats + 1, 1u);
         __syncthreads();
         whole_row<DT, Policy>(sm, p, r, base, n, row);
+        VTS_STAMP(4);
         return;
     }
     const bool rupper = !mixed && tup >= (uint32_t)p.k;
@@ -1724,6 +1768,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         }
         __syncthreads();
         select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, th, rupper ? G.T2 : 0u));
+        VTS_STAMP(4);
         return;
     }
     // Too many for the on-chip slots: this unit's candidates stay in place and
@@ -1742,6 +1787,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     const uint32_t m = sm.cand_n;
     __syncthreads();
     select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, m, rupper ? G.T2 : 0u));
+    VTS_STAMP(4);
 }
 
 }  // namespace vts
