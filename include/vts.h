@@ -48,8 +48,9 @@ typedef enum {
      * (FlashInfer top_k_varlen doc, "raises ValueError"). */
     VTS_ERR_INVALID = -1,
     /* the request is valid but outside what this library implements:
-     * top_k outside [1, 2048], a row of width columns taking 2^31 bytes or
-     * more, or a device other than gfx950. */
+     * top_k above 16384 (above 2048 in the deterministic mode), a row of
+     * width columns taking 2^31 bytes or more, or a device other than
+     * gfx950. */
     VTS_ERR_UNSUPPORTED = -2,
     /* workspace pointer null or smaller than the matching *_workspace_bytes(). */
     VTS_ERR_WORKSPACE = -3,
@@ -90,7 +91,10 @@ int vts_workspace_init(void* workspace, size_t bytes, void* stream);
  *             t = r % next_n-th row and ranks its first
  *               n = max(0, (seq_lens[i] - next_n + t + 1) / compress_ratio)
  *             columns (integer division), clamped to `width`.
- * top_k       1 <= top_k <= 2048.
+ * top_k       1 <= top_k <= 16384 (the range of FlashInfer's radix_filter
+ *             backend, same page, `backend`).  Above 2048 the candidate
+ *             lists live in LDS and the workspace (a larger workspace, see
+ *             vts_topk_varlen_workspace_bytes) instead of registers.
  * next_n      >= 1, must divide num_rows.
  * compress_ratio >= 1.
  * pre_idx     device int32[num_rows / next_n, top_k] or NULL: the previous
@@ -162,7 +166,8 @@ enum vts_tie_break {
  * LARGE choice among tied values).  The order itself is not spelled out there;
  * value descending, then column ascending, is the reading taken here.
  *
- * Arguments, windows, errors and workspace are those of vts_topk_varlen;
+ * Arguments, windows, errors and workspace are those of vts_topk_varlen,
+ * except that top_k is at most 2048 (VTS_ERR_UNSUPPORTED above);
  * tie_break is VTS_TIE_SMALL or VTS_TIE_LARGE, optionally plus
  * VTS_TIE_UNSORTED (anything else: VTS_ERR_INVALID).  The selected set is
  * unique: every value above the k-th largest, then, of the values equal to
@@ -204,7 +209,7 @@ int vts_topk_varlen_ordered(const void* logits, int32_t dtype, int64_t num_rows,
  *              (row_starts, or 0); when page_size > 1 and row_starts is given
  *              it is required.
  * page_size    1 <= page_size <= 2^30.
- * top_k        1 <= top_k <= 2048.
+ * top_k        1 <= top_k <= 16384.
  * out          device int32[num_rows, top_k], 16-byte aligned: for each
  *              selected window-relative index idx,
  *                src_page_table[r, pt_start + idx / page_size] * page_size

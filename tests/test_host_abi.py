@@ -102,7 +102,7 @@ def _varlen(lib, **kw):
     (dict(width=0), INVALID),
     (dict(row_stride=100), INVALID),
     (dict(top_k=0), INVALID),
-    (dict(top_k=2049), UNSUPPORTED),
+    (dict(top_k=16385), UNSUPPORTED),
     (dict(width=1 << 31, row_stride=1 << 31), UNSUPPORTED),
     (dict(width=1 << 29, row_stride=1 << 29), UNSUPPORTED),   # 2^31 bytes of fp32
     (dict(dtype=1, width=1 << 30, row_stride=1 << 30), UNSUPPORTED),
@@ -152,7 +152,7 @@ def _transform(lib, **kw):
     (dict(raw=A + 8), INVALID),
     (dict(raw=A + 1024), INVALID),          # overlaps out (4 x 256 x 4 bytes)
     (dict(scores=A + 1), INVALID),          # not aligned to 2-byte fp16 elements
-    (dict(top_k=4096), UNSUPPORTED),
+    (dict(top_k=16385), UNSUPPORTED),
     (dict(ws_bytes=0), WORKSPACE),
 ])
 def test_transform_argument_errors(lib, kw, want):
@@ -217,3 +217,23 @@ def test_noalloc_rejects_a_shape_beyond_its_scratch_on_the_host(lib):
                                      None)
     assert st == -5
     assert b"scratch" in lib.vts_status_string(st)
+
+
+def test_wide_top_k_limits_and_workspace(lib):
+    # top_k above 2048 takes a larger workspace (candidate slots per unit
+    # scale with top_k); the deterministic mode stops at 2048
+    small = lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0)
+    wide = lib.vts_topk_varlen_workspace_bytes(64, 163840, 16384, 0)
+    assert wide > small
+    assert lib.vts_topk_varlen_workspace_bytes(64, 163840, 4097, 0) == \
+        lib.vts_topk_varlen_workspace_bytes(64, 163840, 8192, 0)
+    assert lib.vts_page_transform_workspace_bytes(8, 4096, 16384, 2) > \
+        lib.vts_page_transform_workspace_bytes(8, 4096, 512, 2)
+    assert lib.vts_topk_varlen_ordered(A, 0, 8, 4096, 4096, A, 2049, 1, 1, None, A, None, A,
+                                       1 << 40, None, 1) == UNSUPPORTED
+    assert lib.vts_topk_page_table_transform_ordered(A, 2, 4, 1024, 1040, A, None, A, 32, 32, None,
+                                                     64, 4096, A, None, A, 1 << 40, None,
+                                                     2) == UNSUPPORTED
+    # the workspace must match the wide size
+    narrow8 = lib.vts_topk_varlen_workspace_bytes(8, 4096, 512, 0)
+    assert _varlen(lib, top_k=8192, ws_bytes=narrow8) == WORKSPACE

@@ -8,8 +8,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libvts.so")
 # compiled separately and in parallel, linked in this order (the first two are
-# the kernels' code objects: any-order kernels, then the deterministic mode)
-SOURCES = ["vts_kernels.hip", "vts_kernels_ordered.hip", "vts_api.hip"]
+# the kernels' code objects: any-order kernels, the deterministic mode, top_k
+# above 2048)
+SOURCES = ["vts_kernels.hip", "vts_kernels_ordered.hip", "vts_kernels_wide.hip", "vts_api.hip"]
 PROBE_LIB = os.path.join(HERE, "libvts_probe.so")
 PROBE_SOURCES = ["vts_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

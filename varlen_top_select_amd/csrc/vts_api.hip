@@ -52,9 +52,9 @@ int32_t plan_nsplit(int64_t num_rows, int64_t width) {
     return (int32_t)ns;
 }
 
-size_t workspace_bytes(int64_t num_rows, int64_t width) {
+size_t workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k) {
     if (num_rows <= 0) return 256;
-    return ws_layout(num_rows, plan_nsplit(num_rows, width)).total;
+    return ws_layout(num_rows, plan_nsplit(num_rows, width), slots_for_k(top_k)).total;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -72,7 +72,7 @@ int check_rows(const void* x, int32_t dtype, int64_t num_rows, int64_t width, in
     if (dtype != VTS_F32 && dtype != VTS_BF16 && dtype != VTS_F16) return VTS_ERR_INVALID;
     if (num_rows < 0 || width < 1 || row_stride < width) return VTS_ERR_INVALID;
     if (top_k < 1) return VTS_ERR_INVALID;
-    if (top_k > 2048) return VTS_ERR_UNSUPPORTED;
+    if (top_k > K_MAX) return VTS_ERR_UNSUPPORTED;
     if (width > INT32_MAX || num_rows > (int64_t)INT32_MAX / MAX_SPLIT) return VTS_ERR_UNSUPPORTED;
     // a row is streamed with 32-bit byte offsets
     if (width * (int64_t)itemsize(dtype) > (int64_t)INT32_MAX) return VTS_ERR_UNSUPPORTED;
@@ -80,9 +80,9 @@ int check_rows(const void* x, int32_t dtype, int64_t num_rows, int64_t width, in
     return VTS_OK;
 }
 
-int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width) {
+int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width, int32_t top_k) {
     if (ws == nullptr || !aligned(ws, 16)) return VTS_ERR_WORKSPACE;
-    if (bytes < workspace_bytes(num_rows, width)) return VTS_ERR_WORKSPACE;
+    if (bytes < workspace_bytes(num_rows, width, top_k)) return VTS_ERR_WORKSPACE;
     return VTS_OK;
 }
 
@@ -142,8 +142,12 @@ int scratch_of(int dev, void** out) {
 // Candidate slots per unit that let the workspace of this shape fit the
 // scratch array (at most HI_SLOTS, in steps of 64), or 0 when even CAP slots
 // per unit -- what a split row's units publish -- do not fit.
-int32_t scratch_slots(int64_t num_rows, int64_t width) {
+int32_t scratch_slots(int64_t num_rows, int64_t width, int32_t top_k) {
     const int32_t ns = plan_nsplit(num_rows, width);
+    if (top_k > NARROW_K_MAX) {  // wide lists need all their slots
+        const int32_t slots = slots_for_k(top_k);
+        return ws_layout(num_rows, ns, slots).total <= SCRATCH_BYTES ? slots : 0;
+    }
     for (int32_t slots = HI_SLOTS; slots >= CAP; slots -= 64)
         if (ws_layout(num_rows, ns, slots).total <= SCRATCH_BYTES) return slots;
     return 0;
@@ -152,7 +156,7 @@ int32_t scratch_slots(int64_t num_rows, int64_t width) {
 // The launch plan and the workspace pointers; `slots` candidate slots per
 // unit in the workspace (>= CAP whenever a row is split: a split row's units
 // publish their on-chip lists there).
-void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots = HI_SLOTS) {
+void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots) {
     const int32_t ns = plan_nsplit(num_rows, width);
     const WsLayout L = ws_layout(num_rows, ns, slots);
     char* w = static_cast<char*>(ws);
@@ -166,7 +170,7 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slo
                  num_rows <= 4 * BALANCE_CUS && g_tune.no_balance == 0)
                     ? 1 : 0;
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
-    p.hi_cap = HI_SLOTS;
+    p.hi_cap = slots;
     if (g_tune.spill_slots > 0) p.hi_cap = g_tune.spill_slots;
     if (p.hi_cap > slots) p.hi_cap = slots;
     if (p.hi_cap < p.lds_cap) p.hi_cap = p.lds_cap;
@@ -199,12 +203,12 @@ bool order_of(int32_t tie_break, int32_t* order) {
 
 extern "C" {
 
-size_t vts_topk_varlen_workspace_bytes(int64_t num_rows, int64_t width, int32_t, int32_t) {
-    return workspace_bytes(num_rows, width);
+size_t vts_topk_varlen_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k, int32_t) {
+    return workspace_bytes(num_rows, width, top_k);
 }
 
-size_t vts_page_transform_workspace_bytes(int64_t num_rows, int64_t width, int32_t, int32_t) {
-    return workspace_bytes(num_rows, width);
+size_t vts_page_transform_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k, int32_t) {
+    return workspace_bytes(num_rows, width, top_k);
 }
 
 int vts_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -237,12 +241,13 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
         pre_idx = nullptr;
         warn = VTS_WARN_HINT_DISCARDED;
     }
-    int32_t slots = HI_SLOTS;
+    if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
+    int32_t slots = slots_for_k(top_k);
     if (use_scratch) {
-        slots = scratch_slots(num_rows, width);
+        slots = scratch_slots(num_rows, width, top_k);
         if (slots == 0) return VTS_ERR_TOO_LARGE;
     } else {
-        st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+        st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
         if (st != VTS_OK) return st;
     }
     int dev = 0;
@@ -329,7 +334,8 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     if (out_raw_indices && !aligned(out_raw_indices, 16)) return VTS_ERR_INVALID;
     const size_t nk = (size_t)num_rows * (size_t)top_k;
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
     if (st != VTS_OK) return st;
     st = check_device(stream);
     if (st != VTS_OK) return st;
@@ -353,7 +359,7 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace);
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k));
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -394,7 +400,8 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     if (out_raw_indices && !aligned(out_raw_indices, 16)) return VTS_ERR_INVALID;
     const size_t nk = (size_t)num_rows * (size_t)top_k;
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
     if (st != VTS_OK) return st;
     st = check_device(stream);
     if (st != VTS_OK) return st;
@@ -415,7 +422,7 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace);
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k));
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -438,7 +445,8 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     if (out_raw_indices && !aligned(out_raw_indices, 16)) return VTS_ERR_INVALID;
     const size_t nk = (size_t)num_rows * (size_t)top_k;
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width);
+    if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
     if (st != VTS_OK) return st;
     st = check_device(stream);
     if (st != VTS_OK) return st;
@@ -461,8 +469,8 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace);
-    const WsLayout L = ws_layout(num_rows, p.nsplit);
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k));
+    const WsLayout L = ws_layout(num_rows, p.nsplit, p.ws_slots);
     int32_t* row_batch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.batch);
     p.row_batch = row_batch;
     hipStream_t s = static_cast<hipStream_t>(stream);

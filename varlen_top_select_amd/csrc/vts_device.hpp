@@ -194,6 +194,11 @@ __device__ __forceinline__ uint32_t wave_ticket_n(uint32_t* counter, uint32_t cn
     return first_lane_value(base) + excl;
 }
 
+// wave_ticket_n for counts of any size (the wide selections enumerate
+// hundreds of entries per thread): the exclusive prefix comes from a DPP scan
+// of the wave.  Every lane of the wave must call it.
+__device__ __forceinline__ uint32_t wave_ticket_any(uint32_t* counter, uint32_t cnt);
+
 // Shared state of one workgroup (at most 40 KB, so four fit on a CU).  The
 // selection histogram and the streaming filter's per-wave staging queues share
 // their space: the queues exist only between two selections, and the
@@ -257,6 +262,15 @@ __device__ __forceinline__ void lds_sync() {
 struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
 struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a < b ? a : b; } };
 struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a > b ? a : b; } };
+
+__device__ __forceinline__ uint32_t wave_ticket_any(uint32_t* counter, uint32_t cnt) {
+    const uint32_t incl = wave_scan(cnt, 0u, OpAdd());
+    const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    if (tot == 0) return 0;  // uniform
+    uint32_t base = 0;
+    if (lane_id() == 0) base = atomicAdd(counter, tot);
+    return first_lane_value(base) + incl - cnt;
+}
 
 // Inclusive prefix sum over the workgroup (thread order).  Contains barriers
 // (LDS-only, as in every helper below): every thread must call it.

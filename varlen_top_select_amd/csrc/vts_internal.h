@@ -14,6 +14,19 @@ namespace vts {
 // where the list spills).
 constexpr int HI_SLOTS = 8192;
 
+// top_k of the kernels that hold a candidate list in registers; larger top_k
+// (up to K_MAX) run the wide kernels, whose lists live in LDS and the
+// workspace (2 * top_k rounded up to a power of two slots per unit).
+constexpr int NARROW_K_MAX = 2048;
+constexpr int K_MAX = 16384;
+
+inline int32_t slots_for_k(int32_t k) {
+    if (k <= NARROW_K_MAX) return HI_SLOTS;
+    int32_t pw = 1;
+    while (pw < k) pw <<= 1;
+    return 2 * pw;
+}
+
 // Compute units of an MI355X: 8 XCDs of 32.  Block b of a launch goes to XCD
 // b % 8, and there the k-th block (b = 8k + x) to compute unit k % 32 while
 // the first blocks fill the device, so blocks k, k + 32, k + 64, ... of an
@@ -105,6 +118,8 @@ inline WsLayout ws_layout(int64_t num_rows, int32_t nsplit, int32_t slots = HI_S
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_varlen_ordered(int dtype, const Params& p, hipStream_t stream);
+hipError_t launch_varlen_wide(int dtype, const Params& p, hipStream_t stream);
+hipError_t launch_transform_wide(int dtype, const Params& p, hipStream_t stream);
 // Zeroes `words` 32-bit words at `p` (a kernel, so it can sit in a captured graph).
 hipError_t launch_zero(uint32_t* p, size_t words, hipStream_t stream);
 hipError_t launch_transform_ordered(int dtype, const Params& p, hipStream_t stream);

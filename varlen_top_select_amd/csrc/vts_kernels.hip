@@ -14,6 +14,7 @@ static hipError_t launch_dt(const Params& p, hipStream_t stream) {
 
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream) {
     if (p.order != ORDER_ANY) return launch_varlen_ordered(dtype, p, stream);
+    if (p.k > NARROW_K_MAX) return launch_varlen_wide(dtype, p, stream);
     switch (dtype) {
         case F32: return launch_dt<F32, VarlenPolicy>(p, stream);
         case BF16: return launch_dt<BF16, VarlenPolicy>(p, stream);
@@ -64,6 +65,7 @@ hipError_t launch_zero(uint32_t* p, size_t words, hipStream_t stream) {
 
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream) {
     if (p.order != ORDER_ANY) return launch_transform_ordered(dtype, p, stream);
+    if (p.k > NARROW_K_MAX) return launch_transform_wide(dtype, p, stream);
     switch (dtype) {
         case F32: return launch_dt<F32, PagePolicy>(p, stream);
         case BF16: return launch_dt<BF16, PagePolicy>(p, stream);

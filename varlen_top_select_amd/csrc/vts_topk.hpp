@@ -1058,6 +1058,93 @@ struct LdsSrc {
     }
 };
 
+// ---------------------------------------------------------------------------
+// wide selections (top_k > 2048): candidate lists too long for the registers
+// are enumerated from LDS and the workspace on every visit
+// ---------------------------------------------------------------------------
+
+constexpr int WIDE_B = 16;  // workspace entries per thread in flight per round
+
+// Visits workspace entries gk[from, n) / gi[from, n), WIDE_B per thread per
+// round with all loads of a round issued before any is used (the entries are
+// in L2: a unit wrote them during its stream).
+template <class F>
+__device__ __forceinline__ void visit_global(const uint32_t* gk, const uint32_t* gi, uint32_t from,
+                                             uint32_t n, F f) {
+    for (uint32_t q0 = from; q0 < n; q0 += (uint32_t)NT * WIDE_B) {
+        uint32_t kk[WIDE_B], cc[WIDE_B];
+#pragma unroll
+        for (int b = 0; b < WIDE_B; ++b) {
+            const uint32_t q = q0 + (uint32_t)b * NT + threadIdx.x;
+            const uint32_t qc = q < n ? q : from;
+            kk[b] = gload(gk + qc);
+            cc[b] = gload(gi + qc);
+        }
+#pragma unroll
+        for (int b = 0; b < WIDE_B; ++b)
+            if (q0 + (uint32_t)b * NT + threadIdx.x < n) f(kk[b], cc[b]);
+    }
+}
+
+// One unit's candidate list: LDS slots [0, own), then its workspace slots
+// [own, n).  Only keys >= thr are visited as selectable.
+struct WideSrc {
+    static constexpr int SLOTS = 0;  // not held in registers
+    uint32_t own, n, thr;
+    const uint32_t* gkey;
+    const uint32_t* gidx;
+    template <class F>
+    __device__ __forceinline__ void for_each(Smem& sm, F f) const {
+        for (uint32_t q = threadIdx.x; q < own; q += NT) {
+            const uint32_t key = sm.key[q];
+            f(key >= thr, key, sm.idx[q]);
+        }
+        visit_global(gkey, gidx, own, n, [&](uint32_t key, uint32_t col) { f(key >= thr, key, col); });
+    }
+};
+
+// The published lists of a split row's units: list q holds sm.seg_hi[q]
+// entries at rkey / ridx + q * stride (every list fits its slots).
+struct MergeSrc {
+    static constexpr int SLOTS = 0;
+    int lists;
+    uint32_t thr, stride;
+    const uint32_t* rkey;
+    const uint32_t* ridx;
+    template <class F>
+    __device__ __forceinline__ void for_each(Smem& sm, F f) const {
+        for (int q = 0; q < lists; ++q)
+            visit_global(rkey + (size_t)q * stride, ridx + (size_t)q * stride, 0u, sm.seg_hi[q],
+                         [&](uint32_t key, uint32_t col) { f(key >= thr, key, col); });
+    }
+};
+
+// Every column of a window, read from the row on every visit: the exact
+// fallback of the wide selections (one HBM pass per visit).
+template <int DT, bool CANON>
+struct RowSrc {
+    static constexpr int SLOTS = 0;
+    const typename Traits<DT>::raw_t* row;
+    uint32_t n;
+    template <class F>
+    __device__ __forceinline__ void for_each(Smem&, F f) const {
+        constexpr int B = 16;
+        for (uint32_t c0 = 0; c0 < n; c0 += (uint32_t)NT * B) {
+            uint32_t v[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint32_t c = c0 + (uint32_t)b * NT + threadIdx.x;
+                v[b] = (uint32_t)gload(row + (c < n ? c : 0u));
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const uint32_t c = c0 + (uint32_t)b * NT + threadIdx.x;
+                if (c < n) f(true, Keys<DT, CANON>::of(v[b]), c);
+            }
+        }
+    }
+};
+
 // Deterministic-mode output of one entry at slot pos: the index through the
 // policy and, for the varlen selection, the value -- the canonical key's own
 // bits, or the element read back from the row where the key stands for
@@ -1239,11 +1326,22 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         ngt += (ok && key > K) ? 1u : 0u;
         neq += (ok && key == K) ? 1u : 0u;
     });
-    uint32_t og = wave_ticket_n(&sm.cnt_a, ngt);
-    uint32_t oe = wave_ticket_n(&sm.cnt_b, neq);
+    // (a wide source can give a thread more entries than wave_ticket_n counts)
+    uint32_t og, oe;
+    if constexpr (Src::SLOTS > 0) {
+        og = wave_ticket_n(&sm.cnt_a, ngt);
+        oe = wave_ticket_n(&sm.cnt_b, neq);
+    } else {
+        og = wave_ticket_any(&sm.cnt_a, ngt);
+        oe = wave_ticket_any(&sm.cnt_b, neq);
+    }
     if constexpr (Policy::GATHERS) {
         const auto w = Policy::row(p, r, base);
-        if (Policy::gathers(p)) {
+        // (sources held in registers only; a wide source translates inline)
+        bool ahead = false;
+        if constexpr (Src::SLOTS > 0) ahead = Policy::gathers(p);
+        if (ahead) {
+          if constexpr (Src::SLOTS > 0) {
             // Every table read of the thread is issued before its first output
             // index store.  Placed after a store, a read would wait for it (the
             // compiler cannot rule out that they overlap, and loads and stores
@@ -1272,6 +1370,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
                 og += isgt ? 1u : 0u;
                 oe += iseq ? 1u : 0u;
             });
+          }
         } else {
             src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
                 const bool isgt = ok && key > K, iseq = ok && key == K;
@@ -1296,10 +1395,10 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
     }
 }
 
-// top_k <= 2048 (the entry points reject more): a short row's outputs fit
-// eight registers per thread
+// A short row (n <= k): the identity, then -1 (and the values, or padding).
+// With a page table each round of SHORT_J slots per thread issues its table
+// reads before any index store.
 constexpr int SHORT_J = 8;
-static_assert(SHORT_J * NT >= 2048, "a short row's outputs fit the registers");
 
 template <int DT, class Policy>
 __device__ __forceinline__ void short_row(const Params& p, int r, int64_t base, int64_t n,
@@ -1307,20 +1406,22 @@ __device__ __forceinline__ void short_row(const Params& p, int r, int64_t base, 
     if constexpr (Policy::GATHERS) {
         // as in select_and_emit: the table reads before the index stores
         const auto w = Policy::row(p, r, base);
-        int32_t tv[SHORT_J];
+        for (int j0 = 0; j0 < p.k; j0 += SHORT_J * NT) {
+            int32_t tv[SHORT_J];
 #pragma unroll
-        for (int u = 0; u < SHORT_J; ++u) {
-            const int j = u * NT + threadIdx.x;
-            tv[u] = -1;
-            if (j < p.k) {
-                Policy::put_raw(p, r, (uint32_t)j, j < n ? j : -1);
-                if (j < n) tv[u] = Policy::translate(p, r, w, j);
+            for (int u = 0; u < SHORT_J; ++u) {
+                const int j = j0 + u * NT + (int)threadIdx.x;
+                tv[u] = -1;
+                if (j < p.k) {
+                    Policy::put_raw(p, r, (uint32_t)j, j < n ? j : -1);
+                    if (j < n) tv[u] = Policy::translate(p, r, w, j);
+                }
             }
-        }
 #pragma unroll
-        for (int u = 0; u < SHORT_J; ++u) {
-            const int j = u * NT + threadIdx.x;
-            if (j < p.k) Policy::put_idx(p, r, (uint32_t)j, tv[u]);
+            for (int u = 0; u < SHORT_J; ++u) {
+                const int j = j0 + u * NT + (int)threadIdx.x;
+                if (j < p.k) Policy::put_idx(p, r, (uint32_t)j, tv[u]);
+            }
         }
     } else {
         for (int j = threadIdx.x; j < p.k; j += NT) {
@@ -1478,7 +1579,9 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     } while (0)
 #endif
 
-template <int DT, class Policy>
+// WIDE: the instantiation for top_k > 2048 (unordered policies only), whose
+// candidate lists outgrow the registers; see the WIDE branch below.
+template <int DT, class Policy, bool WIDE = false>
 __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     using raw_t = typename Traits<DT>::raw_t;
     constexpr bool ORD = Policy::ORDERED;  // deterministic mode: canonical keys
@@ -1548,7 +1651,8 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     Sample<DT> S;
     sample_load<DT>(row, n, spread_hash((uint32_t)r), S);
     u32x4 RA[U], RB[U];
-    bool refiltered = p.force_path == FORCE_CAREFUL;
+    static_assert(!(WIDE && ORD), "the deterministic mode is limited to top_k <= 2048");
+    bool refiltered = !WIDE && p.force_path == FORCE_CAREFUL;
     // (always issued, also where the careful filter will ignore it: straight-line
     // code keeps the wait counts exact)
     const __amdgpu_buffer_rsrc_t rs = body_rsrc(vb, nvec * 16u);
@@ -1608,7 +1712,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         VTS_STAMP(3);
         hist_clear(sm);  // the staging queues overlaid the histogram
         lds_sync();      // everyone has read the counts before they can change
-        if (nh > B.hi_cap) {  // slots ran out: re-filter with compaction
+        if (!WIDE && nh > B.hi_cap) {  // slots ran out: re-filter with compaction
             if (threadIdx.x == 0) gatomic_add(p.ws_stats + 0, 1u);
             refiltered = true;
         }
@@ -1619,6 +1723,90 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
         nh = sm.cand_n;  // every candidate is on chip now
         nup = 0;
         __syncthreads();
+    }
+    if constexpr (WIDE) {
+        // Wide selections keep every candidate (LDS slots, then the unit's
+        // workspace slots: hi_cap covers twice top_k) and select from there.
+        // Exactness still rests on the counts: fewer than k candidates, a
+        // list past its slots or a forced path re-select the row exactly with
+        // radix passes over the row itself (RowSrc).
+        const bool over = nh > B.hi_cap;
+        const bool forced = p.force_path != FORCE_NONE;
+        const uint32_t own = nh < B.lds_cap ? nh : B.lds_cap;
+        const bool upper = nup >= (uint32_t)p.k;
+        if (eff == 1 || direct) {
+            if (nh < (uint32_t)p.k || over || forced) {
+                if (threadIdx.x == 0 && (nh < (uint32_t)p.k || over))
+                    gatomic_add(p.ws_stats + (over ? 0 : 1), 1u);
+                __syncthreads();
+                select_and_emit<DT, Policy>(sm, p, r, base, row, RowSrc<DT, ORD>{row, (uint32_t)n});
+                VTS_STAMP(4);
+                return;
+            }
+            if (threadIdx.x == 0 && !upper) gatomic_add(p.ws_stats + 3, 1u);
+            const uint32_t thr = upper ? G.T2 : 0u;
+            if (nh <= own) {
+                select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, nh, thr));
+            } else {
+                if (threadIdx.x == 0) gatomic_add(p.ws_stats + 2, 1u);
+                select_and_emit<DT, Policy>(sm, p, r, base, row, WideSrc{own, nh, thr, gkey, gidx});
+            }
+            VTS_STAMP(4);
+            return;
+        }
+        // split row: publish the on-chip part behind which the spill already
+        // sits, the counts (bit 31 of the second: the list outgrew its slots),
+        // then the ticket; the last unit selects over all the lists
+        for (uint32_t q = threadIdx.x; q < own; q += NT) {
+            gstore(gkey + q, sm.key[q]);
+            gstore(gidx + q, sm.idx[q]);
+        }
+        if (threadIdx.x == 0) {
+            gstore(p.ws_count + unit, over ? (uint32_t)B.hi_cap : nh);
+            gstore(p.ws_count_up + unit, nup | (over ? 0x80000000u : 0u));
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            const uint32_t old = __hip_atomic_fetch_add((VTS_GLOBAL uint32_t*)(p.ws_ticket + r), 1u,
+                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const bool last = old == (uint32_t)eff - 1u;
+            if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            sm.flag = last ? 1u : 0u;
+        }
+        __syncthreads();
+        VTS_STAMP(5);
+        if (sm.flag == 0) return;
+        const uint32_t unit0 = (uint32_t)r * (uint32_t)p.nsplit;
+        if (threadIdx.x < (unsigned)eff) {
+            sm.seg_hi[threadIdx.x] = gload(p.ws_count + unit0 + threadIdx.x);
+            sm.seg_lo[threadIdx.x] = gload(p.ws_count_up + unit0 + threadIdx.x);
+        }
+        if (threadIdx.x == 0) gstore(p.ws_ticket + r, 0u);  // self-restoring
+        __syncthreads();
+        uint32_t th = 0, tup = 0;
+        bool lost = false;  // some list outgrew its slots
+        for (int q = 0; q < eff; ++q) {
+            th += sm.seg_hi[q];
+            tup += sm.seg_lo[q] & 0x7FFFFFFFu;
+            lost |= (sm.seg_lo[q] >> 31) != 0;
+        }
+        if (th < (uint32_t)p.k || lost || forced) {
+            if (threadIdx.x == 0 && (th < (uint32_t)p.k || lost))
+                gatomic_add(p.ws_stats + (lost ? 0 : 1), 1u);
+            __syncthreads();
+            select_and_emit<DT, Policy>(sm, p, r, base, row, RowSrc<DT, ORD>{row, (uint32_t)n});
+            VTS_STAMP(4);
+            return;
+        }
+        const bool rupper = tup >= (uint32_t)p.k;
+        if (threadIdx.x == 0 && !rupper) gatomic_add(p.ws_stats + 3, 1u);
+        select_and_emit<DT, Policy>(
+            sm, p, r, base, row,
+            MergeSrc{eff, rupper ? G.T2 : 0u, (uint32_t)p.ws_slots, p.ws_key + (size_t)unit0 * (uint32_t)p.ws_slots,
+                     p.ws_idx + (size_t)unit0 * (uint32_t)p.ws_slots});
+        VTS_STAMP(4);
+        return;
     }
     const uint32_t lcap = refiltered ? (uint32_t)CAP : B.lds_cap;
     const uint32_t own = nh < lcap ? nh : lcap;
