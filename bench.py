@@ -277,7 +277,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="long",
                     choices=["small", "dsv32", "long", "dsv4_mtp", "page"])
-    ap.add_argument("--no-hint", action="store_true")
+    ap.add_argument("--no-hint", action="store_true", help="do not pass the workload's hint")
+    ap.add_argument("--hint-rung", action="store_true",
+                    help="bound the threshold by the hint too (diagnostic switch; off by default)")
     ap.add_argument("--cold-reps", type=int, default=30)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true")
@@ -307,6 +309,8 @@ def main() -> int:
     isz = 4 if wl.dtype == 0 else 2
     valid = int(n.sum()) * isz
     alg = algorithmic_bytes(wl, n)
+    if args.hint_rung:
+        vts.set_tuning(vts.TUNE_HINT_RUNG, 1)
     step, ws = make_step(wl, torch, vts, hint=not args.no_hint)
     log(f"warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -353,7 +357,8 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: {wl.rows}x{wl.width} "
                                f"{ {0: 'fp32', 1: 'bf16', 2: 'fp16'}[wl.dtype]}, top_k {wl.k}",
                    "rows": wl.rows, "width": wl.width, "top_k": wl.k,
-                   "hint": (not args.no_hint) and wl.pre_idx is not None,
+                   "hint": ("passed, not read" if not args.hint_rung else "passed, hint rung on")
+                           if (not args.no_hint) and wl.pre_idx is not None else False,
                    "valid_logits_bytes": valid, "parallelism": "1 GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
@@ -396,6 +401,8 @@ def main() -> int:
                            "kernel_frac_of_read_ceiling": round(achieved / ceil, 4)}
     del step, ws
     torch.cuda.empty_cache()
+    if args.hint_rung:
+        vts.set_tuning(vts.TUNE_HINT_RUNG, 0)
 
     if not args.no_others:
         others = {}

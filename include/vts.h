@@ -99,10 +99,13 @@ int vts_workspace_init(void* workspace, size_t bytes, void* stream);
  * compress_ratio >= 1.
  * pre_idx     device int32[num_rows / next_n, top_k] or NULL: the previous
  *             step's selection for each request, a sampling anchor only
- *             (FlashInfer top_k_varlen doc, `pre_idx`).  It is validated (16-byte aligned, else
- *             ignored with VTS_WARN_HINT_DISCARDED) and never read by the
- *             current kernels, which estimate every threshold from a strided
- *             sample of the row.  Results never depend on it.
+ *             (FlashInfer top_k_varlen doc, `pre_idx`).  It is validated
+ *             (16-byte aligned, else ignored with VTS_WARN_HINT_DISCARDED).
+ *             The default path does not read it: its threshold comes from a
+ *             strided sample of the row, which measured faster than also
+ *             bounding it by the hint (the VTS_TUNE_HINT_RUNG switch turns
+ *             that on; it reads the row at every hinted column and the next
+ *             one).  Results never depend on it.
  * out_indices device int32[num_rows, top_k], 16-byte aligned.  Row r receives
  *             the column indices of its top-k (in no particular order) when
  *             n > top_k; the indices 0..n-1 followed by -1 when n <= top_k (all
@@ -348,8 +351,9 @@ const char* vts_status_string(int status);
  *           threshold) was ranked */
 int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* stream);
 
-/* Tuning and test switches (process-wide; not thread-safe).  None of them
- * changes results, only which internal path computes them.
+/* Diagnostic and test switches.  Each applies to the calls (and workspace-size
+ * queries) of the thread that set it, nowhere else.  None of them changes
+ * results, only which internal path computes them.
  *   VTS_TUNE_NSPLIT       workgroups per long row (0 = automatic, 1..32)
  *   VTS_TUNE_FORCE_PATH   0 normal, 1 every chunk uses the compaction filter,
  *                         2 every row is re-selected over the whole row
@@ -366,6 +370,10 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *                         split further (0 = default 32768; 256..2^20)
  *   VTS_TUNE_NO_BALANCE   1 turns off the length-balanced placement of rows on
  *                         compute units (0 = on where it applies)
+ *   VTS_TUNE_HINT_RUNG    1: vts_topk_varlen calls with a pre_idx and top_k
+ *                         <= 2048 also bound the safe threshold from below by the
+ *                         k-th largest value read at the hinted columns
+ *                         (0 = hint not read)
  * The workspace size follows the split count in force when it is queried.
  * Returns VTS_OK or VTS_ERR_INVALID for an unknown key or value. */
 enum {
@@ -376,7 +384,8 @@ enum {
     VTS_TUNE_SAMPLE_SIGMA = 5,
     VTS_TUNE_MIN_CHUNK = 6,
     VTS_TUNE_LIKELY_SIGMA = 7,
-    VTS_TUNE_NO_BALANCE = 8
+    VTS_TUNE_NO_BALANCE = 8,
+    VTS_TUNE_HINT_RUNG = 9
 };
 int vts_set_tuning(int32_t key, int64_t value);
 

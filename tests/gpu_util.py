@@ -38,7 +38,7 @@ def tuning(**kw):
     keys = dict(nsplit=vts.TUNE_NSPLIT, force=vts.TUNE_FORCE_PATH, lds=vts.TUNE_LDS_SLOTS,
                 spill=vts.TUNE_SPILL_SLOTS, sigma=vts.TUNE_SAMPLE_SIGMA,
                 min_chunk=vts.TUNE_MIN_CHUNK, likely=vts.TUNE_LIKELY_SIGMA,
-                no_balance=vts.TUNE_NO_BALANCE)
+                no_balance=vts.TUNE_NO_BALANCE, hint_rung=vts.TUNE_HINT_RUNG)
     try:
         for k, v in kw.items():
             vts.set_tuning(keys[k], v)

@@ -223,3 +223,34 @@ def test_graph_replay_sglang_transforms(variant):
         errs = check_rows(wl.x, wl.dtype, base, n, k, r, ref_raw)
         assert errs == [], f"replay {rep}: " + "\n".join(errs)
         assert np.array_equal(o, want), f"replay {rep}: out is not the translation of the raw indices"
+
+
+def test_capture_without_a_workspace():
+    """workspace=None under capture: a clear error when the capturing stream
+    has no default workspace of that size yet; after one eager call of the
+    shape on that stream, the capture uses the cached one."""
+    wl = workloads.make("small")
+    x = _raw(wl).cuda().view(torch.float32)[:, : wl.width]
+    seq = torch.from_numpy(wl.seq_lens).cuda()
+    idx = torch.empty((wl.rows, wl.k), dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say("capture without a workspace")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        with pytest.raises(RuntimeError, match="workspace"):
+            vts.topk_varlen(x, seq, wl.k, out_indices=idx)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):  # one eager call on the stream that captures
+        vts.topk_varlen(x, seq, wl.k, out_indices=idx)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2, stream=s):
+        vts.topk_varlen(x, seq, wl.k, out_indices=idx)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        assert check_varlen(wl, idx.cpu().numpy(), None) == []

@@ -38,6 +38,17 @@ def test_varlen_workload_full(name):
     _assert_ok(check_varlen(wl, idx, vals))
 
 
+@pytest.mark.parametrize("name", ["dsv32", "long"])
+def test_hint_rung_full(name):
+    """The hinted rung (a diagnostic switch; the default path does not read
+    the hint) at full size, the long batch with the length-balanced placement."""
+    wl = workloads.make(name)
+    say(f"{name} full with the hint rung")
+    with tuning(hint_rung=1):
+        idx, vals, stats = run_varlen(wl)
+    _assert_ok(check_varlen(wl, idx, vals))
+
+
 def test_varlen_long_hint_free():
     wl = workloads.make("long", hint=False)
     say("long full, hint-free")
@@ -239,7 +250,8 @@ def test_poisoned_columns_are_never_selected():
     _assert_ok(check_varlen(wl, idx, v))
 
 
-def test_degenerate_hints():
+@pytest.mark.parametrize("rung", [0, 1])
+def test_degenerate_hints(rung):
     wl = workloads.make("dsv32", rows=8)
     R, k = wl.rows, wl.k
     for name, h in {
@@ -251,9 +263,36 @@ def test_degenerate_hints():
         "random": np.random.default_rng(0).integers(-10, 2 * wl.width, size=(R, k)).astype(np.int32),
     }.items():
         wl.pre_idx = h
-        say(f"hint {name}")
-        idx, v, _ = run_varlen(wl)
+        say(f"hint {name} hint rung {rung}")
+        with tuning(hint_rung=rung):
+            idx, v, _ = run_varlen(wl)
         _assert_ok(check_varlen(wl, idx, v))
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, F16])
+def test_hint_rung_on_cluster_rows(dtype):
+    """The top values sit in one run of 3000 columns; the hint is the previous
+    step's top k (here: the current one shifted left by a column, as if the
+    row had grown by one), so the hint rung is about the k-th largest value.
+    Hinted and hint-free runs are both exact, and the hinted one never needs
+    the whole-row re-selection (its rung is a lower bound of the k-th
+    largest by construction)."""
+    rng = np.random.default_rng(77 + dtype)
+    n_list = [70000, 65536, 40000, 20000]
+    W, k = 70000, 2048
+    vals = _rows_of(n_list, W, rng, "spike_cluster")
+    ref, _, _ = oracle.topk_varlen(vals, F32, np.array(n_list, np.int32), k)
+    hint = np.where(ref > 0, ref - 1, ref).astype(np.int32)
+    wl = _varlen_wl(vals, n_list, k, dtype=dtype, pre_idx=hint)
+    say(f"cluster rows with hint dtype={dtype}")
+    with tuning(hint_rung=1):
+        idx, v, st_hint = run_varlen(wl)
+    _assert_ok(check_varlen(wl, idx, v))
+    say(f"cluster rows without hint dtype={dtype}")
+    idx, v, st_free = run_varlen(wl, use_hint=False)
+    _assert_ok(check_varlen(wl, idx, v))
+    say(f"stats with hint {st_hint}, without {st_free}")
+    assert st_hint[1] == 0
 
 
 # NaN patterns per dtype: sign clear (quiet, payload, signalling), sign set

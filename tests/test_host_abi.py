@@ -166,6 +166,7 @@ def test_tuning_switches(lib):
     assert lib.vts_set_tuning(vts.TUNE_LDS_SLOTS, 10) == INVALID
     assert lib.vts_set_tuning(vts.TUNE_LDS_SLOTS, 3841) == INVALID
     assert lib.vts_set_tuning(vts.TUNE_NO_BALANCE, 2) == INVALID
+    assert lib.vts_set_tuning(vts.TUNE_HINT_RUNG, 2) == INVALID
     for key in (vts.TUNE_NSPLIT, vts.TUNE_FORCE_PATH, vts.TUNE_LDS_SLOTS, vts.TUNE_SPILL_SLOTS,
                 vts.TUNE_SAMPLE_SIGMA, vts.TUNE_NO_BALANCE):
         assert lib.vts_set_tuning(key, 0) == OK
@@ -237,3 +238,19 @@ def test_wide_top_k_limits_and_workspace(lib):
     # the workspace must match the wide size
     narrow8 = lib.vts_topk_varlen_workspace_bytes(8, 4096, 512, 0)
     assert _varlen(lib, top_k=8192, ws_bytes=narrow8) == WORKSPACE
+
+
+def test_tuning_switches_belong_to_the_calling_thread(lib):
+    import threading
+    base = lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0)
+    seen = {}
+
+    def other():
+        assert lib.vts_set_tuning(vts.TUNE_NSPLIT, 1) == OK
+        seen["other"] = lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["other"] < base  # the switch took effect in its own thread ...
+    assert lib.vts_topk_varlen_workspace_bytes(64, 163840, 2048, 0) == base  # ... only there

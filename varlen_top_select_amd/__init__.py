@@ -38,6 +38,7 @@ TUNE_NSPLIT, TUNE_FORCE_PATH, TUNE_LDS_SLOTS, TUNE_SPILL_SLOTS, TUNE_SAMPLE_SIGM
 TUNE_MIN_CHUNK = 6
 TUNE_LIKELY_SIGMA = 7
 TUNE_NO_BALANCE = 8
+TUNE_HINT_RUNG = 9
 
 _DTYPE = {torch.float32: 0, torch.bfloat16: 1, torch.float16: 2}
 
@@ -139,6 +140,12 @@ def _default_workspace(need: int, device, stream_ptr: int) -> torch.Tensor:
     key = (device.index, stream_ptr)
     ws = _WS_CACHE.get(key)
     if ws is None or ws.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            # allocating and zeroing here would record both into the graph
+            raise RuntimeError(
+                "no workspace for this shape on the capturing stream: pass workspace= "
+                "(make_workspace) or make one eager call of this shape on this stream "
+                "before capture")
         ws = torch.empty(need, dtype=torch.uint8, device=device)
         _check("vts_workspace_init", library().vts_workspace_init(ws.data_ptr(), need, stream_ptr))
         _WS_CACHE[key] = ws
@@ -382,7 +389,7 @@ def topk_transform_page1(scores: torch.Tensor, lengths: torch.Tensor, page_table
 
 
 def set_tuning(key: int, value: int) -> None:
-    """Process-wide path switches (see vts_set_tuning in include/vts.h); results never change."""
+    """Path switches of the calling thread (see vts_set_tuning in include/vts.h); results never change."""
     _check("vts_set_tuning", library().vts_set_tuning(key, value))
 
 

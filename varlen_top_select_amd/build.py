@@ -10,7 +10,8 @@ LIB = os.path.join(HERE, "libvts.so")
 # compiled separately and in parallel, linked in this order (the first two are
 # the kernels' code objects: any-order kernels, the deterministic mode, top_k
 # above 2048)
-SOURCES = ["vts_kernels.hip", "vts_kernels_ordered.hip", "vts_kernels_wide.hip", "vts_api.hip"]
+SOURCES = ["vts_kernels.hip", "vts_kernels_ordered.hip", "vts_kernels_wide.hip",
+           "vts_kernels_hint.hip", "vts_api.hip"]
 PROBE_LIB = os.path.join(HERE, "libvts_probe.so")
 PROBE_SOURCES = ["vts_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

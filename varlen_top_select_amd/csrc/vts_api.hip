@@ -26,6 +26,7 @@ constexpr int64_t TARGET_UNITS = 256;
 // the shorter stream (measured on the five benchmark shapes).
 constexpr int32_t MIN_CHUNK = 32768;
 
+// Diagnostic and test switches (vts_set_tuning).
 struct Tuning {
     int32_t nsplit = 0;
     int32_t force_path = 0;
@@ -35,7 +36,11 @@ struct Tuning {
     int32_t min_chunk = 0;
     int32_t likely_tenths = 0;
     int32_t no_balance = 0;
-} g_tune;
+    int32_t hint_rung = 0;
+};
+// per calling thread: a switch set for a test or a measurement changes only
+// the calls (and workspace-size queries) of the thread that set it
+thread_local Tuning g_tune;
 
 #ifdef VTS_PHASE_STAMPS
 uint64_t* g_stamps = nullptr;  // phase-timing build: where the next launches stamp
@@ -275,6 +280,7 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     p.next_n = next_n;
     p.cr = compress_ratio;
     p.pre_idx = pre_idx;
+    p.hint_rung = g_tune.hint_rung;
     p.out_idx = out_indices;
     p.out_vals = out_values;
     p.order = order;
@@ -619,6 +625,10 @@ int vts_set_tuning(int32_t key, int64_t value) {
         case VTS_TUNE_NO_BALANCE:
             if (value < 0 || value > 1) return VTS_ERR_INVALID;
             g_tune.no_balance = (int32_t)value;
+            return VTS_OK;
+        case VTS_TUNE_HINT_RUNG:
+            if (value < 0 || value > 1) return VTS_ERR_INVALID;
+            g_tune.hint_rung = (int32_t)value;
             return VTS_OK;
         case VTS_TUNE_MIN_CHUNK:
             if (value != 0 && (value < 256 || value > (1 << 20))) return VTS_ERR_INVALID;

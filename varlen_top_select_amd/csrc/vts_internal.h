@@ -52,7 +52,8 @@ struct Params {
     const int32_t* seq_lens;
     int32_t next_n;
     int32_t cr;
-    const int32_t* pre_idx;  // reserved for the hint; may be null
+    const int32_t* pre_idx;  // the hint (request-major, k per request), or null
+    int32_t hint_rung;       // 1: bound the safe rung by the hint rung as well (diagnostic)
     // page-transform rows
     const int32_t* lengths;
     const int32_t* row_starts;
@@ -119,6 +120,7 @@ hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_transform(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_varlen_ordered(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_varlen_wide(int dtype, const Params& p, hipStream_t stream);
+hipError_t launch_varlen_hint(int dtype, const Params& p, hipStream_t stream);
 hipError_t launch_transform_wide(int dtype, const Params& p, hipStream_t stream);
 // Zeroes `words` 32-bit words at `p` (a kernel, so it can sit in a captured graph).
 hipError_t launch_zero(uint32_t* p, size_t words, hipStream_t stream);

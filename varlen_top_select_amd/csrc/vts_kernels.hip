@@ -15,6 +15,7 @@ static hipError_t launch_dt(const Params& p, hipStream_t stream) {
 hipError_t launch_varlen(int dtype, const Params& p, hipStream_t stream) {
     if (p.order != ORDER_ANY) return launch_varlen_ordered(dtype, p, stream);
     if (p.k > NARROW_K_MAX) return launch_varlen_wide(dtype, p, stream);
+    if (p.pre_idx && p.hint_rung) return launch_varlen_hint(dtype, p, stream);
     switch (dtype) {
         case F32: return launch_dt<F32, VarlenPolicy>(p, stream);
         case BF16: return launch_dt<BF16, VarlenPolicy>(p, stream);

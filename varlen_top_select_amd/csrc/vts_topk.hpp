@@ -437,6 +437,91 @@ __device__ __forceinline__ Rungs sample_rungs(Smem& sm, const Params& p, int64_t
 }
 
 // ---------------------------------------------------------------------------
+// the hint: the previous step's selection as a sampling anchor
+// ---------------------------------------------------------------------------
+
+// Hint rung (FlashInfer top_k_varlen doc, `pre_idx`: the previous step's top-k
+// of the request, used only as a sampling anchor; GVR V2 keeps it as an
+// anchor of its sampling, exactness never depending on it).  The row's
+// current values are read at every hinted column c and at c + 1 (the pages
+// disagree on a +1 shift between steps; reading both serves either
+// convention): up to 2k reads, each column counted once (one LDS bit per
+// column modulo 2^16 -- a collision only drops a read), hints outside the
+// window ignored.  Any k reads at distinct columns are k elements of the row,
+// so the k-th largest key among them is a lower bound of the row's k-th
+// largest: a rung that never lets fewer than k keys through, and that is
+// close to the k-th largest when the hint overlaps the current top k.
+constexpr int HINT_J = NARROW_K_MAX / NT;       // hint entries per thread (k <= 2048)
+constexpr int HINT_MAP0 = SPREAD_COPIES * SPREAD_STRIDE;  // bitmap after the spread copies
+constexpr int HINT_MAP_WORDS = 2048;            // 2^16 bits
+static_assert(HINT_MAP0 + HINT_MAP_WORDS <= 2 * CAP, "the hint bitmap fits the candidate arrays");
+
+template <int DT>
+struct HintReads {
+    int32_t col[HINT_J];
+    uint32_t key[2 * HINT_J];
+};
+
+// Issues the loads of the hinted columns of request i (the caller waits).
+__device__ __forceinline__ void hint_cols(const Params& p, int i, int32_t (&col)[HINT_J]) {
+    const int32_t* h = p.pre_idx + (int64_t)i * p.k;
+#pragma unroll
+    for (int j = 0; j < HINT_J; ++j) {
+        const int e = j * NT + (int)threadIdx.x;
+        col[j] = e < p.k ? gload(h + e) : -1;
+    }
+}
+
+// Issues the reads of the row at the hinted columns and c + 1.
+template <int DT>
+__device__ __forceinline__ void hint_reads(const typename Traits<DT>::raw_t* row, int64_t n,
+                                           HintReads<DT>& H) {
+#pragma unroll
+    for (int j = 0; j < HINT_J; ++j) {
+        const uint32_t c0 = (uint32_t)H.col[j], c1 = c0 + 1u;
+        const bool v0 = c0 < (uint32_t)n, v1 = v0 && c1 < (uint32_t)n;
+        H.key[2 * j] = v0 ? to_key<DT>(gload(row + c0)) : 0u;
+        H.key[2 * j + 1] = v1 ? to_key<DT>(gload(row + c1)) : 0u;
+    }
+}
+
+// The hint rung from the reads (every thread calls; leaves the spread copies
+// and the bitmap dirty: the caller clears them before the sample select).
+template <int DT>
+__device__ __forceinline__ uint32_t hint_rung(Smem& sm, const Params& p, int64_t n,
+                                              HintReads<DT>& H) {
+    constexpr int BITS = Traits<DT>::BITS;
+    uint32_t* map = sm.cand_words + HINT_MAP0;
+    uint32_t keep = 0;  // bit e: read e is the first read of its column
+#pragma unroll
+    for (int j = 0; j < HINT_J; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t c = (uint32_t)H.col[j] + (uint32_t)h;
+            if ((uint32_t)H.col[j] < (uint32_t)n && c < (uint32_t)n) {
+                const uint32_t b = c & 0xFFFFu, m = 1u << (b & 31u);
+                if (!(atomicOr(&map[b >> 5], m) & m)) keep |= 1u << (2 * j + h);
+            }
+        }
+    }
+    lds_sync();
+    uint32_t t1, t2;
+    block_select_pair<BITS, BITS == 32 ? 9 : BITS - RBITS>(
+        sm,
+        [&](auto f) {
+#pragma unroll
+            for (int e = 0; e < 2 * HINT_J; ++e) f(((keep >> e) & 1u) ? H.key[e] : 0u);
+        },
+        (uint32_t)p.k, (uint32_t)p.k, t1, t2);
+    return t1;
+}
+
+// Zeroes the hint bitmap.
+__device__ __forceinline__ void hint_map_clear(Smem& sm) {
+    for (int j = threadIdx.x; j < HINT_MAP_WORDS; j += NT) sm.cand_words[HINT_MAP0 + j] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // fast filter: one pass, no barriers inside the loop
 // ---------------------------------------------------------------------------
 
@@ -1580,8 +1665,10 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
 #endif
 
 // WIDE: the instantiation for top_k > 2048 (unordered policies only), whose
-// candidate lists outgrow the registers; see the WIDE branch below.
-template <int DT, class Policy, bool WIDE = false>
+// candidate lists outgrow the registers; see the WIDE branch below.  HINT:
+// the instantiation for calls with a hint (varlen, top_k <= 2048), whose
+// safe rung is also bounded below by the hint rung.
+template <int DT, class Policy, bool WIDE = false, bool HINT = false>
 __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     using raw_t = typename Traits<DT>::raw_t;
     constexpr bool ORD = Policy::ORDERED;  // deterministic mode: canonical keys
@@ -1648,8 +1735,14 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
 
     // The sample's loads go out first; the first streaming step's follow once
     // the sample has landed and stay in flight while the rungs are computed.
+    // With a hint, the hinted columns are loaded before the sample and the
+    // row's values at them right after it (those reads need the columns).
+    static_assert(!(HINT && (WIDE || Policy::GATHERS)), "hints serve the varlen selection");
+    HintReads<DT> H;
+    if constexpr (HINT) hint_cols(p, r / p.next_n, H.col);
     Sample<DT> S;
     sample_load<DT>(row, n, spread_hash((uint32_t)r), S);
+    if constexpr (HINT) hint_reads<DT>(row, n, H);
     u32x4 RA[U], RB[U];
     static_assert(!(WIDE && ORD), "the deterministic mode is limited to top_k <= 2048");
     bool refiltered = !WIDE && p.force_path == FORCE_CAREFUL;
@@ -1668,6 +1761,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     }
     hist_clear(sm);    // every select leaves the histogram zeroed again
     spread_clear(sm);  // the sample select's first-pass copies
+    if constexpr (HINT) hint_map_clear(sm);
     lds_sync();        // the loads stay in flight
     // A row that the sample read whole and that fits the on-chip candidate
     // slots is selected directly: its first unit puts every column in the
@@ -1685,7 +1779,19 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     }
     Rungs G{0u, 0u};
     if (!direct) {
+        uint32_t TH = 0u;
+        if constexpr (HINT) {
+            if (!S.whole) {  // (a whole-row sample is exact already)
+                TH = hint_rung<DT>(sm, p, n, H);
+                spread_clear(sm);
+                lds_sync();
+            }
+        }
         G = sample_rungs<DT>(sm, p, n, S, [&]() { load_step(RA, rs, order.first(0, STEP)); });
+        if constexpr (HINT) {  // both rungs are lower bounds of the k-th largest key
+            G.T = G.T > TH ? G.T : TH;
+            G.T2 = G.T2 > TH ? G.T2 : TH;
+        }
         if constexpr (ORD) {  // rungs the canonical keys and the raw-bit tests agree on
             G.T = canon_floor<DT>(G.T);
             G.T2 = canon_floor<DT>(G.T2);
