@@ -11,6 +11,7 @@ phase over the units, in microseconds from the first unit's start.
 
     python -m varlen_top_select_amd.phases --build
     python -m varlen_top_select_amd.phases long dsv32 dsv4_mtp page
+    python -m varlen_top_select_amd.phases --tune resident=1 page   # a switch of vts_set_tuning
 
 The stamped kernel is not the product kernel (the stamps add a few stores);
 the product build never defines the macro.
@@ -78,6 +79,11 @@ def main(argv) -> None:
     if argv and argv[0] == "--build":
         print(build())
         return
+    tune = {}
+    while argv and argv[0] == "--tune":
+        key, val = argv[1].split("=")
+        tune[key] = int(val)
+        argv = argv[2:]
     sys.path.insert(0, ROOT)
     import torch
 
@@ -88,6 +94,8 @@ def main(argv) -> None:
     vts.LIB_PATH = LIB
     lib = vts.library()
     lib.vts_phase_stamps.argtypes = [ctypes.c_void_p]
+    for key, val in tune.items():
+        vts.set_tuning(getattr(vts, "TUNE_" + key.upper()), val)
     for name in argv or ["long", "dsv32", "dsv4_mtp", "page"]:
         wl = workloads.make(name)
         step, ws = bench.make_step(wl, torch, vts)
@@ -108,7 +116,8 @@ def main(argv) -> None:
             b.record()
             torch.cuda.synchronize()
             lib.vts_phase_stamps(None)
-            report(f"{name} {mode}", stamps.cpu().numpy(), a.elapsed_time(b) * 1000.0)
+            label = " ".join([name, mode] + [f"{k}={v}" for k, v in tune.items()])
+            report(label, stamps.cpu().numpy(), a.elapsed_time(b) * 1000.0)
         sys.stdout.flush()
 
 
