@@ -231,6 +231,7 @@ struct Smem {
     uint32_t flag;
     uint32_t total;
     uint32_t win_base, win_n;  // the placed row's window (balanced placement)
+    uint32_t sort_m, sort_r, sort_base;  // deterministic mode: the sort left to the kernel's end
 };
 
 // Inclusive scan across the 64 lanes of a wave with DPP: Hillis-Steele inside

@@ -1284,39 +1284,165 @@ __device__ __forceinline__ void emit_slots(const Params& p, int r, int64_t base,
 }
 
 // Canonical order: sorts LDS slots [0, m) by key descending, then column
-// ascending (a bitonic network over the next power of two, padding slots
-// sorting last), and writes the first m through the policy, then -1 / pad
-// values up to k.
+// ascending, and writes the first m through the policy, then -1 / pad values
+// up to k.  The order is that of the 64-bit word (key << 32) | ~column, sorted
+// descending by a bitonic network over P = NT * E words (E = 1, 2, 4 or 8, the
+// smallest with P >= m; padding words are 0, below every entry).  The network
+// is the form in which every step orders its pairs the same way: merge stage
+// s (blocks of 2^(s+1) positions) first pairs position i with its mirror
+// image i ^ (2^(s+1) - 1), then with i ^ 2^j for j = s-1 .. 0, and the lower
+// position of each pair keeps the larger word.  Thread t keeps positions
+// t*E .. t*E + E - 1 in registers: a pair inside the thread needs no
+// exchange, a pair across lanes of one wave exchanges words by DPP (lanes
+// 1 and 2 apart, mirrors of 4, 8 and 16 lanes) or ds_bpermute, and only
+// pairs across waves pass through LDS.  The network is unrolled into straight
+// code, so the words stay in registers without copies between steps; the
+// kernel inlines it once, in its epilogue (defer_sort).
 static_assert(CAP >= 2048, "a canonical-order sort of up to 2048 entries fits the candidate slots");
+static_assert(NT == 256, "the register sort maps bits 6 and 7 of the thread index to waves");
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_word(uint64_t x) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)x, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(x >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t perm_word(uint64_t x, uint32_t addr) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)(uint32_t)x);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_bpermute((int)addr, (int)(uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int E>
+constexpr int log2_of() {
+    return E == 1 ? 0 : E == 2 ? 1 : E == 4 ? 2 : 3;
+}
+
+// One step of the network.  MIR: pairs i with i ^ (2^(J+1) - 1), else with
+// i ^ 2^J (J counts position bits: bits below log2 E select the register,
+// the next 8 the thread).
+template <int E, int J, bool MIR>
+__device__ __forceinline__ void net_step(Smem& sm, uint64_t (&v)[E], uint32_t t) {
+    constexpr int LE = log2_of<E>();
+    if constexpr (J < LE) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            if (e & (1 << J)) continue;
+            uint64_t& a = v[e];
+            uint64_t& b = v[MIR ? e ^ ((2 << J) - 1) : e | (1 << J)];
+            const bool swap = a < b;
+            const uint64_t hi = swap ? b : a;
+            b = swap ? a : b;
+            a = hi;
+        }
+    } else {
+        // the partner of (t, e) is (t ^ TM, MIR ? E-1-e : e); the lower
+        // position is the one whose thread bit J - LE is clear
+        constexpr uint32_t JT = (uint32_t)(J - LE);
+        constexpr uint32_t TM = MIR ? (2u << JT) - 1u : 1u << JT;
+        const bool keep_max = ((t >> JT) & 1u) == 0;
+        uint64_t o[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const uint64_t x = v[MIR ? E - 1 - e : e];
+            if constexpr (TM == 1) {
+                o[e] = dpp_word<0xB1>(x);  // quad_perm 1,0,3,2
+            } else if constexpr (TM == 2) {
+                o[e] = dpp_word<0x4E>(x);  // quad_perm 2,3,0,1
+            } else if constexpr (TM == 3) {
+                o[e] = dpp_word<0x1B>(x);  // quad_perm 3,2,1,0
+            } else if constexpr (TM == 7) {
+                o[e] = dpp_word<0x141>(x);  // row_half_mirror
+            } else if constexpr (TM == 15) {
+                o[e] = dpp_word<0x140>(x);  // row_mirror
+            } else if constexpr (TM < 64) {
+                o[e] = perm_word(x, ((t & 63u) ^ TM) << 2);
+            }
+        }
+        if constexpr (TM >= 64) {
+            // across waves: every word goes through LDS at [e * NT + t]
+            uint64_t* words = reinterpret_cast<uint64_t*>(sm.cand_words);
+#pragma unroll
+            for (int e = 0; e < E; ++e) words[e * NT + t] = v[e];
+            lds_sync();
+#pragma unroll
+            for (int e = 0; e < E; ++e) o[e] = words[(MIR ? E - 1 - e : e) * NT + (t ^ TM)];
+            lds_sync();
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const bool gt = v[e] > o[e];
+            v[e] = gt == keep_max ? v[e] : o[e];
+        }
+    }
+}
+
+// Half-cleaner steps of strides 2^J .. 1.
+template <int E, int J>
+__device__ __forceinline__ void half_steps(Smem& sm, uint64_t (&v)[E], uint32_t t) {
+    if constexpr (J >= 0) {
+        net_step<E, J, false>(sm, v, t);
+        half_steps<E, J - 1>(sm, v, t);
+    }
+}
+
+// Merge stages S .. log2 P - 1, each its mirror step and then its
+// half-cleaners.
+template <int E, int S>
+__device__ __forceinline__ void stages_from(Smem& sm, uint64_t (&v)[E], uint32_t t) {
+    if constexpr (S < log2_of<E>() + 8) {
+        net_step<E, S, true>(sm, v, t);
+        half_steps<E, S - 1>(sm, v, t);
+        stages_from<E, S + 1>(sm, v, t);
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void sort_slots(Smem& sm, uint32_t m) {
+    const uint32_t t = threadIdx.x;
+    lds_sync();  // the slots were written by other threads
+    uint64_t v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t q = (uint32_t)e * NT + t;
+        v[e] = q < m ? ((uint64_t)sm.key[q] << 32) | (uint32_t)~sm.idx[q] : 0ull;
+    }
+    lds_sync();  // the slots are read before the exchanges reuse their space
+    stages_from<E, 0>(sm, v, threadIdx.x);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const uint32_t q = t * (uint32_t)E + (uint32_t)e;
+        sm.key[q] = (uint32_t)(v[e] >> 32);
+        sm.idx[q] = ~(uint32_t)v[e];
+    }
+    lds_sync();
+}
+
+// Deterministic mode leaves the canonical sort to the kernel's epilogue, so
+// that the network is inlined once per kernel: the m entries wait in LDS
+// slots [0, m) of row r, whose window starts at `base`.
+constexpr uint32_t NO_SORT = 0xFFFFFFFFu;
+
+__device__ __forceinline__ void defer_sort(Smem& sm, int r, int64_t base, uint32_t m) {
+    if (threadIdx.x == 0) {
+        sm.sort_m = m;
+        sm.sort_r = (uint32_t)r;
+        sm.sort_base = (uint32_t)base;  // window starts lie in [0, width], width < 2^31
+    }
+}
 
 template <int DT, class Policy>
 __device__ __forceinline__ void sort_and_emit(Smem& sm, const Params& p, int r, int64_t base,
                                               const typename Traits<DT>::raw_t* row, uint32_t m) {
-    uint32_t P = 1;
-    while (P < m) P <<= 1;
-    for (uint32_t q = m + threadIdx.x; q < P; q += NT) {
-        sm.key[q] = 0u;
-        sm.idx[q] = 0xFFFFFFFFu;  // complement 0: below every column of a key-0 entry
-    }
-    lds_sync();
-    for (uint32_t size = 2; size <= P; size <<= 1) {
-        for (uint32_t stride = size >> 1; stride > 0; stride >>= 1) {
-            for (uint32_t t = threadIdx.x; t < P / 2; t += NT) {
-                const uint32_t i = ((t & ~(stride - 1)) << 1) | (t & (stride - 1));
-                const uint32_t j = i + stride;
-                const uint64_t a = ((uint64_t)sm.key[i] << 32) | (uint32_t)~sm.idx[i];
-                const uint64_t b = ((uint64_t)sm.key[j] << 32) | (uint32_t)~sm.idx[j];
-                const bool down = (i & size) == 0;  // this block ends descending
-                if (down ? a < b : a > b) {
-                    const uint32_t ki = sm.key[i], ii = sm.idx[i];
-                    sm.key[i] = sm.key[j];
-                    sm.idx[i] = sm.idx[j];
-                    sm.key[j] = ki;
-                    sm.idx[j] = ii;
-                }
-            }
-            lds_sync();
-        }
+    if (m <= NT) {
+        sort_slots<1>(sm, m);
+    } else if (m <= 2 * NT) {
+        sort_slots<2>(sm, m);
+    } else if (m <= 4 * NT) {
+        sort_slots<4>(sm, m);
+    } else {
+        sort_slots<8>(sm, m);
     }
     emit_slots<DT, Policy>(p, r, base, row, [&](uint32_t q, int32_t& col, uint32_t& key) {
         const bool in = q < m;
@@ -1376,7 +1502,7 @@ __device__ __forceinline__ void ordered_emit(Smem& sm, const Params& p, int r, i
             ++o;
         }
     });
-    sort_and_emit<DT, Policy>(sm, p, r, base, row, (uint32_t)p.k);
+    defer_sort(sm, r, base, (uint32_t)p.k);
 }
 
 // Selects the top k of `src` (which must hold at least k entries and contain
@@ -1668,17 +1794,10 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
 // candidate lists outgrow the registers; see the WIDE branch below.  HINT:
 // the instantiation for calls with a hint (varlen, top_k <= 2048), whose
 // safe rung is also bounded below by the hint rung.
-template <int DT, class Policy, bool WIDE = false, bool HINT = false>
-__global__ void __launch_bounds__(NT) topk_kernel(Params p) {
+template <int DT, class Policy, bool WIDE, bool HINT>
+__device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bid, uint32_t unit) {
     using raw_t = typename Traits<DT>::raw_t;
     constexpr bool ORD = Policy::ORDERED;  // deterministic mode: canonical keys
-    __shared__ Smem sm;
-
-    // units of one row are consecutive and land on one XCD (dispatch is
-    // round-robin over the 8 XCDs by block index)
-    const uint32_t bid = blockIdx.x;
-    const uint32_t unit = (bid & 7u) * (uint32_t)p.units_per_xcd + (bid >> 3);
-    if (unit >= (uint32_t)p.num_units) return;
     VTS_STAMP(0);
     // The row and its window are the same in every lane, but they arrive
     // through LDS and vector loads; readfirstlane puts them in scalar
@@ -1709,7 +1828,7 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
                     sm.key[j] = Keys<DT, ORD>::of((uint32_t)gload(row + j));
                     sm.idx[j] = (uint32_t)j;
                 }
-                sort_and_emit<DT, Policy>(sm, p, r, base, row, (uint32_t)n);
+                defer_sort(sm, r, base, (uint32_t)n);
             } else {
                 short_row<DT, Policy>(p, r, base, n, row);
             }
@@ -2082,6 +2201,31 @@ __global__ void __launch_bounds__(NT) topk_kernel(Params p) {
     __syncthreads();
     select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, m, rupper ? G.T2 : 0u));
     VTS_STAMP(4);
+}
+
+template <int DT, class Policy, bool WIDE = false, bool HINT = false>
+__global__ void __launch_bounds__(NT) topk_kernel(Params p) {
+    __shared__ Smem sm;
+    // units of one row are consecutive and land on one XCD (dispatch is
+    // round-robin over the 8 XCDs by block index)
+    const uint32_t bid = blockIdx.x;
+    const uint32_t unit = (bid & 7u) * (uint32_t)p.units_per_xcd + (bid >> 3);
+    if (unit >= (uint32_t)p.num_units) return;
+    if constexpr (Policy::ORDERED) {
+        if (threadIdx.x == 0) sm.sort_m = NO_SORT;
+    }
+    topk_unit<DT, Policy, WIDE, HINT>(sm, p, bid, unit);
+    if constexpr (Policy::ORDERED) {
+        lds_sync();
+        const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.sort_m);
+        if (m != NO_SORT) {
+            const int r = __builtin_amdgcn_readfirstlane((int)sm.sort_r);
+            const int64_t base = __builtin_amdgcn_readfirstlane((int)sm.sort_base);
+            const auto* row = static_cast<const typename Traits<DT>::raw_t*>(p.x) + (int64_t)r * p.row_stride + base;
+            sort_and_emit<DT, Policy>(sm, p, r, base, row, m);
+            VTS_STAMP(4);
+        }
+    }
 }
 
 }  // namespace vts
