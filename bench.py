@@ -19,7 +19,7 @@ Prints ONE JSON line:
   cpu_baseline the CPU oracle timed on a bounded sample of the same batch
   others      µs/call of the other four workloads (smaller, latency-bound)
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 10]
 """
 from __future__ import annotations
 
@@ -85,8 +85,10 @@ def upload(wl, torch):
     return raw.view(dt)[:, : wl.width], dt
 
 
-def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False, page1: bool = False):
-    """Returns (step, out tensors, workspace) for one call of the whole batch."""
+def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False, page1: bool = False,
+              tie: str | None = None):
+    """Returns (step, workspace) for one call of the whole batch (with `tie`,
+    the deterministic mode of the varlen selection)."""
     x, dt = upload(wl, torch)
     R, k = wl.rows, wl.k
     if wl.kind == "varlen":
@@ -97,9 +99,15 @@ def make_step(wl, torch, vts, hint: bool = True, ragged: bool = False, page1: bo
         ws = vts.make_workspace(R, wl.width, k, dt, "cuda")
 
         def step():
-            vts.topk_varlen(x, seq, k, pre_idx=pre, compress_ratio=wl.compress_ratio,
-                            next_n=wl.next_n, return_values=wl.return_values, out_indices=idx,
-                            out_values=vals, workspace=ws)
+            if tie is None:
+                vts.topk_varlen(x, seq, k, pre_idx=pre, compress_ratio=wl.compress_ratio,
+                                next_n=wl.next_n, return_values=wl.return_values, out_indices=idx,
+                                out_values=vals, workspace=ws)
+            else:
+                vts.topk_varlen_ordered(x, seq, k, tie_break=tie, pre_idx=pre,
+                                        compress_ratio=wl.compress_ratio, next_n=wl.next_n,
+                                        return_values=wl.return_values, out_indices=idx,
+                                        out_values=vals, workspace=ws)
         return step, ws
     L = torch.from_numpy(wl.lengths).cuda()
     rs = torch.from_numpy(wl.row_starts).cuda()
@@ -274,13 +282,13 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long",
                     choices=["small", "dsv32", "long", "dsv4_mtp", "page"])
     ap.add_argument("--no-hint", action="store_true", help="do not pass the workload's hint")
     ap.add_argument("--hint-rung", action="store_true",
                     help="bound the threshold by the hint too (diagnostic switch; off by default)")
-    ap.add_argument("--cold-reps", type=int, default=30)
+    ap.add_argument("--cold-reps", type=int, default=100)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only-steps", action="store_true",
@@ -406,17 +414,23 @@ def main() -> int:
 
     if not args.no_others:
         others = {}
-        for name in ("small", "dsv32", "long", "dsv4_mtp", "page", "page_ragged", "page_page1"):
+        for name in ("small", "dsv32", "long", "dsv4_mtp", "page", "page_ragged", "page_page1",
+                     "long_ordered", "dsv4_mtp_ordered", "long_k16384"):
             if name == args.workload:
                 continue
             log(f"workload {name}")
-            w2 = workloads.make(name.split("_")[0] if name.startswith("page") else name)
+            base_name = name.split("_")[0] if name.startswith(("page", "long")) else name
+            base_name = "dsv4_mtp" if name.startswith("dsv4_mtp") else base_name
+            w2 = workloads.make(base_name)
+            if name == "long_k16384":  # top_k at the end of radix_filter's range
+                w2.k, w2.pre_idx = 16384, None
             n2 = valid_lengths(w2)
             s2, ws2 = make_step(w2, torch, vts, ragged=name.endswith("_ragged"),
-                                page1=name.endswith("_page1"))
-            for _ in range(5):
+                                page1=name.endswith("_page1"),
+                                tie="small" if name.endswith("_ordered") else None)
+            for _ in range(10):
                 s2()
-            ct2 = cold_times(s2, torch, 20)
+            ct2 = cold_times(s2, torch, args.cold_reps)
             vb2 = int(n2.sum()) * (4 if w2.dtype == 0 else 2)
             others[name] = {
                 "us_median_cold": round(float(np.median(ct2)), 2),
