@@ -365,6 +365,33 @@ def test_transform_identity_page_size_1_no_starts():
     assert np.array_equal(out, raw)
 
 
+@pytest.mark.parametrize("page_size", [1, 16, 32, 48, 64])
+def test_transform_page_sizes_and_table_edges(page_size):
+    """Page sizes on both sides of the output translation's LDS staging (a
+    power-of-two page size and at most 2560 pages per window; 32 stages 2048
+    pages, the first 1024 read ahead of the count and the rest after it; 16
+    has 4096 pages and 48 is no power of two, both read the table per entry),
+    page-table row starts below zero and tables narrower than the windows, so
+    that some pages fall outside the table at either end."""
+    wl = workloads.make("page", rows=24)
+    W = wl.width
+    g = np.random.default_rng(500 + page_size)
+    wl.page_size = page_size
+    pages = -(-W // page_size)
+    cols = 3000 if page_size == 1 else pages - pages // 8
+    wl.page_table = g.integers(0, 1 << 20, size=(wl.rows, cols), dtype=np.int32)
+    wl.page_table_row_starts = g.integers(-40, 40, size=wl.rows).astype(np.int32)
+    lengths = np.array([W, W, 60000, 40000, 2048, 2049, 2500, 2600, 3000, 100, 64 * 2560,
+                        64 * 1024 + 5, 0, 1, 70000, 33333, 20000, 10000, 5000, 4097, 4096, 2047,
+                        65, 64], np.int64)
+    wl.lengths[:] = np.minimum(lengths, W).astype(np.int32)
+    wl.row_starts[:] = np.array([0 if wl.lengths[i] >= W else int(g.integers(0, W - wl.lengths[i] + 1))
+                                 for i in range(wl.rows)], np.int32)
+    say(f"transform page_size {page_size}, table of {cols} columns")
+    out, raw, _ = run_transform(wl)
+    _assert_ok(check_transform_wl(wl, out, raw))
+
+
 def test_transform_without_raw_output():
     wl = workloads.make("page", rows=8)
     say("transform without out_raw")

@@ -217,6 +217,8 @@ struct Smem {
             u32x4 vec[WAVES * STAGE];  // wave w owns [w * STAGE, (w + 1) * STAGE)
             uint32_t v[WAVES * STAGE];  // the vectors' indices in the unit's body
         } stage;
+        // after the last selection: the page-table entries of the row's window
+        uint32_t table[WAVES * STAGE * 5];
     };
     uint32_t wsum[WAVES];
     uint32_t wmin[WAVES];
@@ -232,7 +234,11 @@ struct Smem {
     uint32_t total;
     uint32_t win_base, win_n;  // the placed row's window (balanced placement)
     uint32_t sort_m, sort_r, sort_base;  // deterministic mode: the sort left to the kernel's end
+    uint32_t row_n;  // the unit's row: valid columns of its window
 };
+
+constexpr int TABLE_WORDS = WAVES * STAGE * 5;
+static_assert(sizeof(((Smem*)nullptr)->table) == sizeof(((Smem*)nullptr)->stage), "the table fills the staging area");
 
 // Inclusive scan across the 64 lanes of a wave with DPP: Hillis-Steele inside
 // each 16-lane row (row_shr 1, 2, 4, 8), then row_bcast 15 and 31 carry the

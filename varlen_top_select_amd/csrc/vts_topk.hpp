@@ -52,6 +52,14 @@ namespace vts {
 // row windows and output policies
 // ---------------------------------------------------------------------------
 
+// A row's page-table entries [start, start + np) staged in LDS: table[j]
+// holds table column start + j for j in [jlo, jhi), the pages that lie inside
+// the table; the page size is 2^sh.
+struct StagedTable {
+    const uint32_t* table;
+    uint32_t jlo, jhi, sh;
+};
+
 struct VarlenPolicy {
     // the output needs no memory reads of its own
     static constexpr bool GATHERS = false;
@@ -163,6 +171,43 @@ struct PagePolicy {
         if (pc < 0 || pc >= p.pt_width) return -1;
         const int64_t page = gload(p.pt + (int64_t)r * p.pt_stride + pc);
         return (int32_t)(page * p.page_size + col % p.page_size);
+    }
+    // Pages of a window of n columns under a table whose page size P is a
+    // power of two (0 where the translation reads no such table): window
+    // column c maps to table column start + c / P.
+    __device__ __forceinline__ static uint32_t table_pages(const Params& p, int64_t n) {
+        if (p.offsets || p.row_batch || (p.page_size & (p.page_size - 1)) != 0) return 0;
+        return (uint32_t)((n + p.page_size - 1) / p.page_size);
+    }
+    __device__ __forceinline__ static StagedTable staged(const Params& p, const Row& w, const uint32_t* table,
+                                                    uint32_t np) {
+        const int64_t lo = w.start < 0 ? -w.start : 0;
+        const int64_t hi = p.pt_width - w.start;
+        StagedTable t;
+        t.table = table;
+        t.jlo = (uint32_t)(lo < (int64_t)np ? lo : (int64_t)np);
+        t.jhi = (uint32_t)(hi < (int64_t)t.jlo ? (int64_t)t.jlo : (hi < (int64_t)np ? hi : (int64_t)np));
+        t.sh = (uint32_t)__builtin_ctz((uint32_t)p.page_size);
+        return t;
+    }
+    // Issues this thread's loads of the staged entries j = u * NT + thread.
+    template <int TJ>
+    __device__ __forceinline__ static void table_fetch(const Params& p, int r, const Row& w, const StagedTable& t,
+                                                       uint32_t (&tl)[TJ]) {
+#pragma unroll
+        for (int u = 0; u < TJ; ++u) {
+            const uint32_t j = (uint32_t)u * NT + threadIdx.x;
+            tl[u] = 0u;
+            if (j >= t.jlo && j < t.jhi) tl[u] = (uint32_t)gload(p.pt + (int64_t)r * p.pt_stride + w.start + j);
+        }
+    }
+    // translate from the staged entries (the same bits: the low 32 bits of
+    // page * P + col % P)
+    __device__ __forceinline__ static int32_t translate_staged(const StagedTable& t, int32_t col) {
+        if (col < 0) return -1;
+        const uint32_t j = (uint32_t)col >> t.sh;
+        if (j < t.jlo || j >= t.jhi) return -1;
+        return (int32_t)((t.table[j] << t.sh) + ((uint32_t)col & ((1u << t.sh) - 1u)));
     }
     // output slot pos: the raw index col, and the translated index t
     __device__ __forceinline__ static void put_raw(const Params& p, int r, uint32_t pos, int32_t col) {
@@ -1524,6 +1569,24 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         return;
     }
     const uint32_t need_eq = (uint32_t)p.k - gt;
+    // With a page table whose entries for the row's window fit the staging
+    // area (free now that the selections are done), they go to LDS and the
+    // translation reads no global memory between the output stores.  The
+    // first TJ * NT entries are read here and land while the outputs are
+    // counted; the rest of a longer window are read after the count.
+    constexpr int TJ = 4;
+    [[maybe_unused]] uint32_t tl[TJ];
+    uint32_t np = 0;
+    [[maybe_unused]] StagedTable stg{};
+    if constexpr (Policy::GATHERS && Src::SLOTS > 0) {
+        np = Policy::table_pages(p, (uint32_t)__builtin_amdgcn_readfirstlane((int)sm.row_n));
+        if (np > (uint32_t)TABLE_WORDS) np = 0;
+        if (np) {
+            const auto w = Policy::row(p, r, base);
+            stg = Policy::staged(p, w, sm.table, np);
+            Policy::template table_fetch<TJ>(p, r, w, stg, tl);
+        }
+    }
     if (threadIdx.x == 0) {
         sm.cnt_a = 0;
         sm.cnt_b = 0;
@@ -1551,6 +1614,16 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         // (sources held in registers only; a wide source translates inline)
         bool ahead = false;
         if constexpr (Src::SLOTS > 0) ahead = Policy::gathers(p);
+        if (np) {
+#pragma unroll
+            for (int u = 0; u < TJ; ++u) {
+                const uint32_t j = (uint32_t)u * NT + threadIdx.x;
+                if (j < np) sm.table[j] = tl[u];
+            }
+            for (uint32_t j = (uint32_t)TJ * NT + threadIdx.x; j < np; j += NT)
+                sm.table[j] = j >= stg.jlo && j < stg.jhi ? (uint32_t)gload(p.pt + (int64_t)r * p.pt_stride + w.start + j) : 0u;
+            lds_sync();
+        }
         if (ahead) {
           if constexpr (Src::SLOTS > 0) {
             // Every table read of the thread is issued before its first output
@@ -1559,28 +1632,45 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
             // share one completion counter), one memory round trip per register.
             // The first pass also writes the raw indices, so the registers that
             // held them take the translated ones and the pass adds none.
-            const uint32_t og0 = og, oe0 = oe;
-            int32_t tv[Src::SLOTS];
-            src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t col) {
-                const bool isgt = ok && key > K, iseq = ok && key == K;
-                const uint32_t pos = isgt ? og : gt + oe;
-                tv[j] = -1;
-                if (isgt || (iseq && oe < need_eq)) {
-                    Policy::put_raw(p, r, pos, (int32_t)col);
-                    tv[j] = Policy::translate(p, r, w, (int32_t)col);
-                }
-                og += isgt ? 1u : 0u;
-                oe += iseq ? 1u : 0u;
-            });
-            og = og0;
-            oe = oe0;
-            src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t) {
-                const bool isgt = ok && key > K, iseq = ok && key == K;
-                const uint32_t pos = isgt ? og : gt + oe;
-                if (isgt || (iseq && oe < need_eq)) Policy::put_idx(p, r, pos, tv[j]);
-                og += isgt ? 1u : 0u;
-                oe += iseq ? 1u : 0u;
-            });
+            auto two_passes = [&](auto translate) {
+                const uint32_t og0 = og, oe0 = oe;
+                int32_t tv[Src::SLOTS];
+                src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t col) {
+                    const bool isgt = ok && key > K, iseq = ok && key == K;
+                    const uint32_t pos = isgt ? og : gt + oe;
+                    tv[j] = -1;
+                    if (isgt || (iseq && oe < need_eq)) {
+                        Policy::put_raw(p, r, pos, (int32_t)col);
+                        tv[j] = translate((int32_t)col);
+                    }
+                    og += isgt ? 1u : 0u;
+                    oe += iseq ? 1u : 0u;
+                });
+                og = og0;
+                oe = oe0;
+                src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t) {
+                    const bool isgt = ok && key > K, iseq = ok && key == K;
+                    const uint32_t pos = isgt ? og : gt + oe;
+                    if (isgt || (iseq && oe < need_eq)) Policy::put_idx(p, r, pos, tv[j]);
+                    og += isgt ? 1u : 0u;
+                    oe += iseq ? 1u : 0u;
+                });
+            };
+            if (np) {
+                // the translation reads LDS only: one pass
+                src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+                    const bool isgt = ok && key > K, iseq = ok && key == K;
+                    const uint32_t pos = isgt ? og : gt + oe;
+                    if (isgt || (iseq && oe < need_eq)) {
+                        Policy::put_raw(p, r, pos, (int32_t)col);
+                        Policy::put_idx(p, r, pos, Policy::translate_staged(stg, (int32_t)col));
+                    }
+                    og += isgt ? 1u : 0u;
+                    oe += iseq ? 1u : 0u;
+                });
+            } else {
+                two_passes([&](int32_t col) { return Policy::translate(p, r, w, col); });
+            }
           }
         } else {
             src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
@@ -1818,6 +1908,7 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     n = __builtin_amdgcn_readfirstlane((int)n);
     VTS_STAMP(1);
     VTS_STAMP_ID(r, n);
+    if (threadIdx.x == 0) sm.row_n = (uint32_t)n;
     const raw_t* row = static_cast<const raw_t*>(p.x) + (int64_t)r * p.row_stride + base;
     if (n <= p.k) {
         if (c == 0) {
