@@ -63,7 +63,7 @@ typedef enum {
 
 /* Workspace: device scratch used by rows that several workgroups share and by
  * candidate overflow.  Query its size with the matching *_workspace_bytes()
- * (a pure host function of the shape), allocate it, fill it with zeros ONCE
+ * (a pure host function of the shape and element type), allocate it, fill it with zeros ONCE
  * (vts_workspace_init or any memset), then pass it to every call of that
  * shape.  Each call leaves it as it found it apart from the event counters of
  * vts_workspace_stats, so it never needs clearing again.  One workspace must

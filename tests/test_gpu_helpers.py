@@ -1,0 +1,122 @@
+"""GPU parity of the second workgroups that the length-balanced placement of
+512 rows gives to rows far longer than the batch's mean (at least 256 KB of
+window and more than twice the mean; only the 128 longest rows can take one).
+
+Two length profiles: "few" -- a handful of long rows around the 256 KB bound
+(one element short of it, exactly on it, one past it) among short rows -- and
+"many" -- 200 long rows, so that rows of rank 128 and beyond qualify by length
+but must stay whole.  Every case prints its name before its GPU step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads.synth import F16, F32, BF16, Workload, to_bf16_bits, to_f16_bits
+from tests.gpu_util import (check_transform_wl, check_varlen, run_transform, run_varlen, say,
+                            tuning)
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+R = 512
+W = 196608  # at least 256 KB of fp32, fp16 and bf16 columns
+
+
+def _split_cols(dtype):
+    return (256 * 1024) // (4 if dtype == F32 else 2)
+
+
+def _lengths(profile, dtype, rng):
+    n = rng.integers(100, 3001, size=R).astype(np.int64)
+    s = _split_cols(dtype)
+    if profile == "few":
+        special = [W, s, s - 1, s + 1, (s + W) // 2, W - 7, 2 * s if 2 * s <= W else W - 1]
+        at = rng.choice(R, size=len(special), replace=False)
+        n[at] = special
+    else:
+        at = rng.choice(R, size=200, replace=False)
+        n[at] = W - rng.integers(0, 64, size=200)
+    return n
+
+
+def _bits(rng, dtype):
+    v = rng.standard_normal((R, W), dtype=np.float32)
+    if dtype == F32:
+        return v.view(np.uint32)
+    return to_bf16_bits(v) if dtype == BF16 else to_f16_bits(v)
+
+
+def _varlen(profile, dtype, k, seed):
+    rng = np.random.default_rng(seed)
+    n = _lengths(profile, dtype, rng)
+    return Workload(name=f"helpers-{profile}", kind="varlen", dtype=dtype, x=_bits(rng, dtype),
+                    width=W, k=k, seq_lens=n.astype(np.int32), next_n=1, compress_ratio=1,
+                    pre_idx=None, return_values=True)
+
+
+def _expected_splits(wl):
+    n = np.minimum(wl.seq_lens.astype(np.int64), W)
+    mean2 = 2 * int((n >> 10).sum())
+    qual = (n >= _split_cols(wl.dtype)) & ((n >> 10) * R >= mean2)
+    order = np.argsort(-n, kind="stable")
+    return int(qual[order[:128]].sum()), int(qual.sum())
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16, F16])
+@pytest.mark.parametrize("profile", ["few", "many"])
+def test_helpers_varlen(profile, dtype):
+    wl = _varlen(profile, dtype, 2048, 700 + dtype + (10 if profile == "many" else 0))
+    split, qual = _expected_splits(wl)
+    say(f"helpers varlen {profile} dtype {dtype}: {split} rows split, {qual} qualify")
+    assert split > 0
+    idx, vals, _ = run_varlen(wl)
+    errs = check_varlen(wl, idx, vals)
+    assert errs == [], "\n".join(errs[:8])
+    say("the same without the balanced placement (no second workgroups)")
+    with tuning(no_balance=1):
+        idx2, vals2, _ = run_varlen(wl)
+    errs = check_varlen(wl, idx2, vals2)
+    assert errs == [], "\n".join(errs[:8])
+
+
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("profile", ["few", "many"])
+def test_helpers_ordered(profile, dtype):
+    wl = _varlen(profile, dtype, 1024, 800 + dtype + (10 if profile == "many" else 0))
+    say(f"helpers ordered (SMALL) {profile} dtype {dtype}")
+    idx, vals, _ = run_varlen(wl, tie="small")
+    ref_idx, ref_vals, _ = oracle.topk_varlen_ordered(wl.x[:, :W], wl.dtype, wl.seq_lens, wl.k,
+                                                      "small", return_values=True)
+    bad = np.argwhere(idx != ref_idx)
+    assert bad.size == 0, f"indices differ at {bad[:4].tolist()}"
+    assert np.array_equal(vals, ref_vals), "values differ"
+
+
+def test_helpers_wide():
+    wl = _varlen("few", BF16, 4096, 901)
+    say("helpers varlen top_k 4096 (wide kernels), bf16")
+    idx, vals, _ = run_varlen(wl)
+    errs = check_varlen(wl, idx, vals)
+    assert errs == [], "\n".join(errs[:8])
+
+
+def test_helpers_page_transform():
+    rng = np.random.default_rng(902)
+    dtype = F16
+    n = _lengths("few", dtype, rng)
+    starts = np.array([rng.integers(0, W - m + 1) for m in n], np.int64)
+    P = W // 64 + 16
+    wl = Workload(name="helpers-page", kind="transform", dtype=dtype, x=_bits(rng, dtype),
+                  width=W, k=2048)
+    wl.lengths = n.astype(np.int32)
+    wl.row_starts = starts.astype(np.int32)
+    wl.page_size = 64
+    wl.page_table = rng.permutation(R * P).astype(np.int32).reshape(R, P)
+    wl.page_table_row_starts = rng.integers(0, 16, size=R).astype(np.int32)
+    say("helpers page transform, fp16, page 64")
+    out, raw, _ = run_transform(wl)
+    errs = check_transform_wl(wl, out, raw)
+    assert errs == [], "\n".join(errs[:8])

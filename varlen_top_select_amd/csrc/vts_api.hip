@@ -46,9 +46,30 @@ thread_local Tuning g_tune;
 uint64_t* g_stamps = nullptr;  // phase-timing build: where the next launches stamp
 #endif
 
-int32_t plan_nsplit(int64_t num_rows, int64_t width) {
+size_t itemsize(int32_t dtype) { return dtype == VTS_F32 ? 4 : 2; }
+
+// With the length-balanced placement of 2 * BALANCE_CUS rows (two per compute
+// unit), the rows far longer than the batch's mean (more than twice it, and
+// at least LONG_ROW_BYTES) take a second workgroup on a compute unit of their
+// own: one workgroup's stream is capped by the memory requests its compute
+// unit keeps in flight (~20 GB/s), so such a row would otherwise finish long
+// after the rest.  A split pays a second sample and a merge (~8 us), which a
+// stream of 256 KB or more at that rate outweighs (measured on DSv4 MTP:
+// 34.6 against 41.5 us cold; splitting rows of 192 or 128 KB, or every row
+// above 64 KB in four, was slower).  The rows are known only on the device,
+// which decides per row; the plan reserves the workgroups and workspace.
+constexpr int64_t LONG_ROW_BYTES = 256 * 1024;
+
+int32_t split_cols(int32_t dtype) { return (int32_t)(LONG_ROW_BYTES / (int64_t)itemsize(dtype)); }
+
+bool helpers_apply(int64_t num_rows, int64_t width, int32_t dtype) {
+    return num_rows == 2 * BALANCE_CUS && width >= split_cols(dtype) && g_tune.no_balance == 0;
+}
+
+int32_t plan_nsplit(int64_t num_rows, int64_t width, int32_t dtype) {
     if (g_tune.nsplit > 0) return g_tune.nsplit;
     if (num_rows <= 0) return 1;
+    if (helpers_apply(num_rows, width, dtype)) return 2;
     int64_t ns = (TARGET_UNITS + num_rows - 1) / num_rows;
     const int64_t by_width = (width + MIN_CHUNK - 1) / MIN_CHUNK;
     if (ns > by_width) ns = by_width;
@@ -57,9 +78,9 @@ int32_t plan_nsplit(int64_t num_rows, int64_t width) {
     return (int32_t)ns;
 }
 
-size_t workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k) {
+size_t workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k, int32_t dtype) {
     if (num_rows <= 0) return 256;
-    return ws_layout(num_rows, plan_nsplit(num_rows, width), slots_for_k(top_k)).total;
+    return ws_layout(num_rows, plan_nsplit(num_rows, width, dtype), slots_for_k(top_k)).total;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -68,8 +89,6 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
     return a0 < b0 + nb && b0 < a0 + na;
 }
-
-size_t itemsize(int32_t dtype) { return dtype == VTS_F32 ? 4 : 2; }
 
 // Common checks of the score-row arguments.
 int check_rows(const void* x, int32_t dtype, int64_t num_rows, int64_t width, int64_t row_stride,
@@ -85,9 +104,10 @@ int check_rows(const void* x, int32_t dtype, int64_t num_rows, int64_t width, in
     return VTS_OK;
 }
 
-int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width, int32_t top_k) {
+int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width, int32_t top_k,
+                    int32_t dtype) {
     if (ws == nullptr || !aligned(ws, 16)) return VTS_ERR_WORKSPACE;
-    if (bytes < workspace_bytes(num_rows, width, top_k)) return VTS_ERR_WORKSPACE;
+    if (bytes < workspace_bytes(num_rows, width, top_k, dtype)) return VTS_ERR_WORKSPACE;
     return VTS_OK;
 }
 
@@ -147,8 +167,8 @@ int scratch_of(int dev, void** out) {
 // Candidate slots per unit that let the workspace of this shape fit the
 // scratch array (at most HI_SLOTS, in steps of 64), or 0 when even CAP slots
 // per unit -- what a split row's units publish -- do not fit.
-int32_t scratch_slots(int64_t num_rows, int64_t width, int32_t top_k) {
-    const int32_t ns = plan_nsplit(num_rows, width);
+int32_t scratch_slots(int64_t num_rows, int64_t width, int32_t top_k, int32_t dtype) {
+    const int32_t ns = plan_nsplit(num_rows, width, dtype);
     if (top_k > NARROW_K_MAX) {  // wide lists need all their slots
         const int32_t slots = slots_for_k(top_k);
         return ws_layout(num_rows, ns, slots).total <= SCRATCH_BYTES ? slots : 0;
@@ -161,8 +181,8 @@ int32_t scratch_slots(int64_t num_rows, int64_t width, int32_t top_k) {
 // The launch plan and the workspace pointers; `slots` candidate slots per
 // unit in the workspace (>= CAP whenever a row is split: a split row's units
 // publish their on-chip lists there).
-void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots) {
-    const int32_t ns = plan_nsplit(num_rows, width);
+void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots, int32_t dtype) {
+    const int32_t ns = plan_nsplit(num_rows, width, dtype);
     const WsLayout L = ws_layout(num_rows, ns, slots);
     char* w = static_cast<char*>(ws);
     p.nsplit = ns;
@@ -171,8 +191,10 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slo
     p.units_per_xcd = (p.num_units + 7) / 8;
     // length-balanced row placement: one workgroup per row, whole slots on all
     // 256 CUs (2..4 rows per CU, all resident at once)
-    p.balance = (ns == 1 && num_rows % BALANCE_CUS == 0 && num_rows >= 2 * BALANCE_CUS &&
-                 num_rows <= 4 * BALANCE_CUS && g_tune.no_balance == 0)
+    p.helpers = ns == 2 && g_tune.nsplit == 0 && helpers_apply(num_rows, width, dtype) ? 1 : 0;
+    p.split_cols = split_cols(dtype);
+    p.balance = ((ns == 1 && num_rows % BALANCE_CUS == 0 && num_rows >= 2 * BALANCE_CUS &&
+                  num_rows <= 4 * BALANCE_CUS && g_tune.no_balance == 0) || p.helpers)
                     ? 1 : 0;
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
     p.hi_cap = slots;
@@ -208,12 +230,14 @@ bool order_of(int32_t tie_break, int32_t* order) {
 
 extern "C" {
 
-size_t vts_topk_varlen_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k, int32_t) {
-    return workspace_bytes(num_rows, width, top_k);
+size_t vts_topk_varlen_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k,
+                                       int32_t dtype) {
+    return workspace_bytes(num_rows, width, top_k, dtype);
 }
 
-size_t vts_page_transform_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k, int32_t) {
-    return workspace_bytes(num_rows, width, top_k);
+size_t vts_page_transform_workspace_bytes(int64_t num_rows, int64_t width, int32_t top_k,
+                                          int32_t dtype) {
+    return workspace_bytes(num_rows, width, top_k, dtype);
 }
 
 int vts_workspace_init(void* workspace, size_t bytes, void* stream) {
@@ -249,10 +273,10 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
     int32_t slots = slots_for_k(top_k);
     if (use_scratch) {
-        slots = scratch_slots(num_rows, width, top_k);
+        slots = scratch_slots(num_rows, width, top_k, dtype);
         if (slots == 0) return VTS_ERR_TOO_LARGE;
     } else {
-        st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
+        st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
         if (st != VTS_OK) return st;
     }
     int dev = 0;
@@ -263,7 +287,7 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
         if (st != VTS_OK) return st;
         // the scratch keeps the last call's contents, which may have another
         // layout: clear the counters and row tickets, which must start at zero
-        const WsLayout L = ws_layout(num_rows, plan_nsplit(num_rows, width), slots);
+        const WsLayout L = ws_layout(num_rows, plan_nsplit(num_rows, width, dtype), slots);
         if (launch_zero(static_cast<uint32_t*>(workspace), L.count / 4,
                         static_cast<hipStream_t>(stream)) != hipSuccess)
             return VTS_ERR_HIP;
@@ -284,7 +308,7 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     p.out_idx = out_indices;
     p.out_vals = out_values;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots);
+    fill_plan(p, num_rows, width, workspace, slots, dtype);
     if (launch_varlen(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess) return VTS_ERR_HIP;
     return warn;
 }
@@ -341,7 +365,7 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     const size_t nk = (size_t)num_rows * (size_t)top_k;
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
     if (st != VTS_OK) return st;
     st = check_device(stream);
     if (st != VTS_OK) return st;
@@ -365,7 +389,7 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k));
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -407,7 +431,7 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     const size_t nk = (size_t)num_rows * (size_t)top_k;
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
     if (st != VTS_OK) return st;
     st = check_device(stream);
     if (st != VTS_OK) return st;
@@ -428,7 +452,7 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k));
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -452,7 +476,7 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     const size_t nk = (size_t)num_rows * (size_t)top_k;
     if (out_raw_indices && overlap(out, nk * 4, out_raw_indices, nk * 4)) return VTS_ERR_INVALID;
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
-    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k);
+    st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
     if (st != VTS_OK) return st;
     st = check_device(stream);
     if (st != VTS_OK) return st;
@@ -475,7 +499,7 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k));
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype);
     const WsLayout L = ws_layout(num_rows, p.nsplit, p.ws_slots);
     int32_t* row_batch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.batch);
     p.row_batch = row_batch;

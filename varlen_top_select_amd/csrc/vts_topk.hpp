@@ -1753,11 +1753,13 @@ __device__ __forceinline__ void whole_row(Smem& sm, const Params& p, int r, int6
 // same number of columns and no unit is left with only long rows.  Every
 // workgroup derives the same ranking from the row lengths, and the map from
 // blocks to ranks is a bijection, so each row is taken exactly once; the
-// placement only changes speed.  The row's window comes back in base / n.
+// placement only changes speed.  The row's window comes back in base / n, the
+// workgroup's unit of the row in c (0; 1 for a second workgroup of a split
+// row; -1: nothing to do) and the row's unit count in eff (see below).
 // Every thread must call it.
 template <class Policy>
 __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t bid,
-                                            int64_t& base, int64_t& n) {
+                                            int64_t& base, int64_t& n, int& c, int& eff) {
     constexpr int NB = 32;
     constexpr int MAXPER = 4;  // rows per thread (R <= 4 * NT)
     const int per = p.num_rows / NT;
@@ -1772,27 +1774,72 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     for (int i = 0; i < MAXPER; ++i)
         raw[i] = Policy::fetch(p, i < per ? (int)threadIdx.x + i * NT : 0);
     const float scale = (float)NB / (float)(p.width + 1);
+    uint32_t ksum = 0;  // this thread's rows: valid columns / 1024, summed (exact)
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
         int64_t b, n;
         Policy::finish(p, (int)threadIdx.x + i * NT, raw[i], b, n);
         wb[i] = (uint32_t)b;
         wn[i] = (uint32_t)n;
+        ksum += i < per ? wn[i] >> 10 : 0u;
         uint32_t q = (uint32_t)((float)n * scale);  // 0..NB-1, longer rows higher
         q = q > NB - 1 ? NB - 1 : q;
         bk[i] = i < per ? NB - 1 - q : (uint32_t)NB;  // 0: longest; NB: no row
     }
+    uint32_t* ktot = sm.hist + NB;  // sum of every row's valid columns / 1024
     if (threadIdx.x < NB) cnt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) sm.total = 0xFFFFFFFFu;
+    if (threadIdx.x == 0) {
+        sm.total = 0xFFFFFFFFu;
+        *ktot = 0;
+    }
     lds_sync();
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i)
         if (i < per) atomicAdd(&cnt[bk[i]], 1u);
+    {
+        const uint32_t wk = wave_scan(ksum, 0u, OpAdd());  // (< 2^31: width < 2^31, R <= 1024)
+        if (lane_id() == 63) atomicAdd(ktot, wk);
+    }
     lds_sync();
-    const uint32_t x = bid % BALANCE_XCDS, k = bid / BALANCE_XCDS;
-    const uint32_t g = x * BALANCE_CUS_PER_XCD + k % BALANCE_CUS_PER_XCD;
-    const uint32_t j = k / BALANCE_CUS_PER_XCD;
-    const uint32_t rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
+    // Workgroup bid < R lands on compute unit k % 32 of XCD x (bid = 8k + x),
+    // numbered g = 32 x + k % 32 -- or, with helpers, g = 8 (k % 32) + x, so
+    // that consecutive numbers alternate over the XCDs and the longest rows
+    // spread over all of them (measured: the contiguous numbering is 2 us
+    // faster on 1024 rows, the alternating one 3 us faster on DSv4 MTP with
+    // helpers) -- and in round j = k / 32 it takes the row of rank j * 256 + g
+    // (even rounds) or j * 256 + 255 - g (odd rounds; rank 0: the longest), a
+    // serpentine that gives every compute unit a long row and a short one.
+    // With helpers (R = 2 * BALANCE_CUS: two rows per compute unit, room for
+    // as many workgroups again), workgroup
+    // R + 128 + h (h < HELPER_RANKS = 128) -- which lands on compute unit
+    // g = 128 + h, on the XCD of the row of rank h, beside rows of ranks
+    // 128 + h and 383 - h -- is the second unit of the row of rank h, if that
+    // row is split; the other workgroups past R have nothing to do.  A row of
+    // rank < HELPER_RANKS is split in two when its window holds at least
+    // split_cols columns and more than twice the batch's mean: both of its
+    // workgroups decide this from the same integers.
+    static_assert(HELPER_RANKS == 128 && BALANCE_CUS == 256 && BALANCE_XCDS == 8,
+                  "helper slots R + 128 + h land on compute unit number 128 + h");
+    uint32_t rank;
+    c = 0;
+    if (bid < (uint32_t)p.num_rows) {
+        const uint32_t x = bid % BALANCE_XCDS, k = bid / BALANCE_XCDS;
+        const uint32_t g = p.helpers ? (k % BALANCE_CUS_PER_XCD) * BALANCE_XCDS + x
+                                     : x * BALANCE_CUS_PER_XCD + k % BALANCE_CUS_PER_XCD;
+        const uint32_t j = k / BALANCE_CUS_PER_XCD;
+        rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
+    } else {
+        const uint32_t i = bid - (uint32_t)p.num_rows;
+        if (!p.helpers || i < (uint32_t)HELPER_RANKS || i >= 2u * HELPER_RANKS) {
+            c = -1;  // (uniform) no role
+            eff = 1;
+            base = 0;
+            n = 0;
+            return 0;
+        }
+        rank = i - (uint32_t)HELPER_RANKS;
+        c = 1;
+    }
     // bucket holding the rank and the rank within it (the same in every
     // thread): lane b scans bucket b's count, the first lane whose running
     // total passes the rank names it
@@ -1837,7 +1884,10 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     const int row = (int)sm.total;
     base = sm.win_base;
     n = sm.win_n;
-    lds_sync();  // sm.total is rewritten later
+    const bool split = p.helpers && rank < (uint32_t)HELPER_RANKS && n >= p.split_cols &&
+                       (uint64_t)((uint32_t)n >> 10) * (uint64_t)p.num_rows >= 2ull * *ktot;
+    eff = split ? 2 : 1;
+    lds_sync();  // sm.total and the histogram are rewritten later
     if (row >= 0 && row < p.num_rows) return row;
     const int r = (int)(bid % (uint32_t)p.num_rows);  // not reached: the map is a bijection
     Policy::window(p, r, base, n);
@@ -1894,15 +1944,17 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     // registers, so the stream's buffer offsets are scalar and its loads need
     // no per-lane loop.
     int64_t base, n;
-    int r;
+    int r, c = 0, beff = 1;
     if (p.balance) {
-        r = balanced_row<Policy>(sm, p, bid, base, n);
+        r = balanced_row<Policy>(sm, p, bid, base, n, c, beff);
+        c = __builtin_amdgcn_readfirstlane(c);
+        if (c < 0) return;  // a helper slot without a row
     } else {
         r = (int)(unit / (uint32_t)p.nsplit);
         Policy::window(p, r, base, n);
     }
     r = __builtin_amdgcn_readfirstlane(r);
-    const int c = p.balance ? 0 : (int)(unit - (uint32_t)r * (uint32_t)p.nsplit);
+    if (!p.balance) c = (int)(unit - (uint32_t)r * (uint32_t)p.nsplit);
     // window starts and lengths lie in [0, width], width < 2^31
     base = __builtin_amdgcn_readfirstlane((int)base);
     n = __builtin_amdgcn_readfirstlane((int)n);
@@ -1930,8 +1982,12 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     int64_t eff64 = (n + p.min_chunk - 1) / p.min_chunk;
     if (eff64 > p.nsplit) eff64 = p.nsplit;
     if (eff64 < 1) eff64 = 1;
-    const int eff = (int)eff64;
+    const int eff = p.balance ? __builtin_amdgcn_readfirstlane(beff) : (int)eff64;
     if (c >= eff) return;
+    // a placed row that may be split has units r * nsplit + c, as elsewhere
+    // (the split-row merge finds the lists and counts there); other placed
+    // rows keep their workgroup's own unit
+    if (p.helpers) unit = (uint32_t)r * (uint32_t)p.nsplit + (uint32_t)c;
 
     const Slice s = make_slice<DT>(row, n, c, eff);
     uint32_t* gkey = p.ws_key + (size_t)unit * (uint32_t)p.ws_slots;
