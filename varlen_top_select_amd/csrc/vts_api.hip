@@ -112,10 +112,11 @@ int check_workspace(void* ws, size_t bytes, int64_t num_rows, int64_t width, int
 }
 
 // The device that work on `stream` runs on (the current device for the null
-// stream), checked to be a gfx950, the result cached per device.
-int check_device(void* stream, int* dev_out = nullptr) {
+// stream), checked to be a gfx950, and its compute units; cached per device.
+int check_device(void* stream, int* dev_out = nullptr, int* cus_out = nullptr) {
     static std::mutex mu;
     static int known[64];  // 0 unknown, 1 gfx950, 2 other
+    static int cus[64];
     int dev = 0;
     if (stream == nullptr) {
         if (hipGetDevice(&dev) != hipSuccess) return VTS_ERR_HIP;
@@ -132,7 +133,9 @@ int check_device(void* stream, int* dev_out = nullptr) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return VTS_ERR_HIP;
         known[dev] = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        cus[dev] = prop.multiProcessorCount;
     }
+    if (cus_out) *cus_out = cus[dev];
     return known[dev] == 1 ? VTS_OK : VTS_ERR_UNSUPPORTED;
 }
 
@@ -181,8 +184,17 @@ int32_t scratch_slots(int64_t num_rows, int64_t width, int32_t top_k, int32_t dt
 // The launch plan and the workspace pointers; `slots` candidate slots per
 // unit in the workspace (>= CAP whenever a row is split: a split row's units
 // publish their on-chip lists there).
-void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots, int32_t dtype) {
-    const int32_t ns = plan_nsplit(num_rows, width, dtype);
+// `cus`: the device's compute units.  The length-balanced placement (and its
+// second workgroups) assumes the dispatch order of 8 XCDs of 32 compute units
+// (BALANCE_CUS); on any other device the rows run in order, one unit each
+// where the plan reserved two (the workspace, sized from the shape alone, is
+// then larger than needed).
+void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slots, int32_t dtype,
+               int cus) {
+    const bool placed = cus == BALANCE_CUS && g_tune.no_balance == 0;
+    int32_t ns = plan_nsplit(num_rows, width, dtype);
+    const bool helpers = ns == 2 && g_tune.nsplit == 0 && helpers_apply(num_rows, width, dtype);
+    if (helpers && !placed) ns = 1;
     const WsLayout L = ws_layout(num_rows, ns, slots);
     char* w = static_cast<char*>(ws);
     p.nsplit = ns;
@@ -191,10 +203,10 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slo
     p.units_per_xcd = (p.num_units + 7) / 8;
     // length-balanced row placement: one workgroup per row, whole slots on all
     // 256 CUs (2..4 rows per CU, all resident at once)
-    p.helpers = ns == 2 && g_tune.nsplit == 0 && helpers_apply(num_rows, width, dtype) ? 1 : 0;
+    p.helpers = helpers && placed ? 1 : 0;
     p.split_cols = split_cols(dtype);
     p.balance = ((ns == 1 && num_rows % BALANCE_CUS == 0 && num_rows >= 2 * BALANCE_CUS &&
-                  num_rows <= 4 * BALANCE_CUS && g_tune.no_balance == 0) || p.helpers)
+                  num_rows <= 4 * BALANCE_CUS && placed) || p.helpers)
                     ? 1 : 0;
     p.lds_cap = g_tune.lds_slots > 0 ? g_tune.lds_slots : CAP;
     p.hi_cap = slots;
@@ -279,8 +291,8 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
         st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
         if (st != VTS_OK) return st;
     }
-    int dev = 0;
-    st = check_device(stream, &dev);
+    int dev = 0, cus = 0;
+    st = check_device(stream, &dev, &cus);
     if (st != VTS_OK) return st;
     if (use_scratch) {
         st = scratch_of(dev, &workspace);
@@ -308,7 +320,7 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     p.out_idx = out_indices;
     p.out_vals = out_values;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots, dtype);
+    fill_plan(p, num_rows, width, workspace, slots, dtype, cus);
     if (launch_varlen(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess) return VTS_ERR_HIP;
     return warn;
 }
@@ -367,7 +379,8 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
     st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
     if (st != VTS_OK) return st;
-    st = check_device(stream);
+    int cus = 0;
+    st = check_device(stream, nullptr, &cus);
     if (st != VTS_OK) return st;
 
     Params p;
@@ -389,7 +402,7 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype);
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype, cus);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -433,7 +446,8 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
     st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
     if (st != VTS_OK) return st;
-    st = check_device(stream);
+    int cus = 0;
+    st = check_device(stream, nullptr, &cus);
     if (st != VTS_OK) return st;
 
     Params p;
@@ -452,7 +466,7 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype);
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype, cus);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -478,7 +492,8 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     if (order != ORDER_ANY && top_k > NARROW_K_MAX) return VTS_ERR_UNSUPPORTED;
     st = check_workspace(workspace, workspace_bytes_, num_rows, width, top_k, dtype);
     if (st != VTS_OK) return st;
-    st = check_device(stream);
+    int cus = 0;
+    st = check_device(stream, nullptr, &cus);
     if (st != VTS_OK) return st;
 
     Params p;
@@ -499,7 +514,7 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     p.out_idx = out;
     p.out_raw = out_raw_indices;
     p.order = order;
-    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype);
+    fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype, cus);
     const WsLayout L = ws_layout(num_rows, p.nsplit, p.ws_slots);
     int32_t* row_batch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.batch);
     p.row_batch = row_batch;
