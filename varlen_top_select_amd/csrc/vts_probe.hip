@@ -1,7 +1,8 @@
 // vts_probe.hip -- two plain streaming kernels used only to calibrate
 // measurements of the top-k kernels on the same device:
-//   vts_probe_read  reads a buffer once with 16-byte loads (the achievable
-//                   read-bandwidth ceiling for the same bytes);
+//   vts_probe_read  reads a buffer once with 16-byte non-temporal loads (the
+//                   achievable read-bandwidth ceiling for the same bytes; the
+//                   hint, which the top-k stream uses too, is worth about 12 %);
 //   vts_probe_copy  copies a buffer with 16-byte loads and stores (a kernel of
 //                   known traffic, to scale the FETCH_SIZE / WRITE_SIZE counters).
 #include <hip/hip_runtime.h>
@@ -28,7 +29,7 @@ __global__ void __launch_bounds__(PT) read_kernel(const v4u* __restrict__ p_, si
 #pragma unroll
         for (int u = 0; u < PU; ++u) {
             const size_t i = base + (size_t)u * PT;
-            v[u] = i < nvec ? p[i] : v4u{0u, 0u, 0u, 0u};
+            v[u] = i < nvec ? __builtin_nontemporal_load(p + i) : v4u{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int u = 0; u < PU; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
