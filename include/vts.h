@@ -351,6 +351,11 @@ const char* vts_status_string(int status);
  *           threshold) was ranked */
 int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* stream);
 
+/* Plan log: with VTS_LOG=1 in the environment (read once per process), every
+ * call prints one line to stderr naming the entry point, the shape, the
+ * kernels (any-order, ordered, wide or hinted), the units per row, the row
+ * placement and the device's compute units.  Results never depend on it. */
+
 /* Diagnostic and test switches.  Each applies to the calls (and workspace-size
  * queries) of the thread that set it, nowhere else.  None of them changes
  * results, only which internal path computes them.

@@ -3,6 +3,9 @@
 Every case prints its name before its GPU step.  Outputs are compared with the
 tie-aware checker (oracle/check.py): bit-exact up to interchangeable ties.
 """
+import os
+import subprocess
+import sys
 import zlib
 
 import numpy as np
@@ -411,3 +414,22 @@ def test_transform_odd_windows():
     say("transform odd windows")
     out, raw, _ = run_transform(wl)
     _assert_ok(check_transform_wl(wl, out, raw))
+
+
+def test_plan_log():
+    """VTS_LOG=1: each call prints the plan it launches, one line on stderr."""
+    code = ("import torch, varlen_top_select_amd as vts\n"
+            "x = torch.randn(4, 4096, device='cuda')\n"
+            "s = torch.tensor([4096, 100, 3000, 1], dtype=torch.int32, device='cuda')\n"
+            "vts.topk_varlen(x, s, 512)\n"
+            "vts.topk_varlen_ordered(x, s, 512)\n"
+            "torch.cuda.synchronize()\n")
+    say("plan log in a child process")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], env=dict(os.environ, VTS_LOG="1"), cwd=root,
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stderr.splitlines() if l.startswith("[vts]")]
+    assert len(lines) == 2, r.stderr[-2000:]
+    assert "vts_topk_varlen: rows 4 width 4096 top_k 512 f32 | kernels any-order" in lines[0]
+    assert "vts_topk_varlen_ordered:" in lines[1] and "kernels ordered" in lines[1]

@@ -1,6 +1,8 @@
 // vts_api.hip -- C ABI of the top-k library: argument checks (host only, before
 // any HIP call), the launch plan (a pure function of the static shape, so a
 // call can be captured in a HIP graph), workspace sizing and the launch.
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <mutex>
@@ -229,6 +231,32 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slo
 #endif
 }
 
+// VTS_LOG=1 in the environment (read once): every call prints the plan it
+// launches to stderr, one line.  Diagnostics only; results never depend on it.
+bool log_on() {
+    static const bool on = [] {
+        const char* v = getenv("VTS_LOG");
+        return v != nullptr && v[0] != '\0' && strcmp(v, "0") != 0;
+    }();
+    return on;
+}
+
+void log_plan(const char* entry, const Params& p, int32_t dtype, int64_t width, int cus) {
+    if (!log_on()) return;
+    static const char* const dts[] = {"f32", "bf16", "f16"};
+    const char* kind = p.order != ORDER_ANY ? "ordered"
+                       : p.k > NARROW_K_MAX ? "wide"
+                       : (p.pre_idx && p.hint_rung) ? "hinted"
+                       : "any-order";
+    fprintf(stderr,
+            "[vts] %s: rows %d width %lld top_k %d %s | kernels %s | units %d (%d per row%s) | "
+            "placement %s | order %d | workspace slots %d per unit | device CUs %d\n",
+            entry, p.num_rows, (long long)width, p.k, dtype >= 0 && dtype < 3 ? dts[dtype] : "?",
+            kind, p.num_units, p.nsplit,
+            p.helpers ? ", the second only for rows far longer than the mean" : "",
+            p.balance ? "length-balanced" : "in row order", p.order, p.ws_slots, cus);
+}
+
 // tie_break argument -> internal order (false: invalid)
 bool order_of(int32_t tie_break, int32_t* order) {
     const int32_t tb = tie_break & ~VTS_TIE_UNSORTED;
@@ -321,6 +349,9 @@ static int topk_varlen_impl(const void* logits, int32_t dtype, int64_t num_rows,
     p.out_vals = out_values;
     p.order = order;
     fill_plan(p, num_rows, width, workspace, slots, dtype, cus);
+    log_plan(use_scratch ? "vts_topk_varlen_noalloc"
+             : order != ORDER_ANY ? "vts_topk_varlen_ordered" : "vts_topk_varlen",
+             p, dtype, width, cus);
     if (launch_varlen(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess) return VTS_ERR_HIP;
     return warn;
 }
@@ -403,6 +434,7 @@ static int page_transform_impl(const void* scores, int32_t dtype, int64_t num_ro
     p.out_raw = out_raw_indices;
     p.order = order;
     fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype, cus);
+    log_plan(p.order != ORDER_ANY ? "vts_topk_page_table_transform_ordered" : "vts_topk_page_table_transform", p, dtype, width, cus);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -467,6 +499,7 @@ static int ragged_impl(const void* scores, int32_t dtype, int64_t num_rows, int6
     p.out_raw = out_raw_indices;
     p.order = order;
     fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype, cus);
+    log_plan(p.order != ORDER_ANY ? "vts_topk_transform_ragged_ordered" : "vts_topk_transform_ragged", p, dtype, width, cus);
     if (launch_transform(dtype, p, static_cast<hipStream_t>(stream)) != hipSuccess)
         return VTS_ERR_HIP;
     return VTS_OK;
@@ -515,6 +548,7 @@ static int page1_impl(const void* scores, int32_t dtype, int64_t num_rows, int64
     p.out_raw = out_raw_indices;
     p.order = order;
     fill_plan(p, num_rows, width, workspace, slots_for_k(top_k), dtype, cus);
+    log_plan(p.order != ORDER_ANY ? "vts_topk_transform_page1_ordered" : "vts_topk_transform_page1", p, dtype, width, cus);
     const WsLayout L = ws_layout(num_rows, p.nsplit, p.ws_slots);
     int32_t* row_batch = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + L.batch);
     p.row_batch = row_batch;
