@@ -638,8 +638,8 @@ int vts_topk_transform_page1_ordered(const void* scores, int32_t dtype, int64_t 
 }
 
 #ifdef VTS_PHASE_STAMPS
-// Phase-timing build only: launches after this call write 8 stamps per unit
-// (row unit u at stamps[8u .. 8u + 7]) into `stamps` (device, or null: off).
+// Phase-timing build only: launches after this call write 16 stamps per unit
+// (row unit u at stamps[16u .. 16u + 15]) into `stamps` (device, or null: off).
 void vts_phase_stamps(void* stamps) { g_stamps = static_cast<uint64_t*>(stamps); }
 #endif
 

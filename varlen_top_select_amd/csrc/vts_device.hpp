@@ -235,6 +235,9 @@ struct Smem {
     uint32_t win_base, win_n;  // the placed row's window (balanced placement)
     uint32_t sort_m, sort_r, sort_base;  // deterministic mode: the sort left to the kernel's end
     uint32_t row_n;  // the unit's row: valid columns of its window
+#ifdef VTS_PHASE_STAMPS
+    uint32_t stamp_unit;  // phase-timing build: the unit whose stamps this workgroup writes
+#endif
 };
 
 constexpr int TABLE_WORDS = WAVES * STAGE * 5;
@@ -356,10 +359,11 @@ __device__ __forceinline__ void hist_clear(Smem& sm) {
 // zeroes the bins.  Lane l sums digits 64*PER-1-PER*l down to 64*PER-PER*(l+1);
 // a DPP scan and a ballot name the lane where the count crosses r, then PER
 // lanes read that lane's bins once more and a second scan names the digit.
+// b1 receives the count of digit d1 itself.
 template <int PER>
 __device__ __forceinline__ void hist_crossing(Smem& sm, uint32_t base, uint32_t r1, uint32_t r2,
                                               uint32_t& d1, uint32_t& a1, uint32_t& d2,
-                                              uint32_t& a2) {
+                                              uint32_t& a2, uint32_t& b1) {
     constexpr uint32_t NB = 64u * PER;
     const uint32_t l = lane_id();
     uint32_t sum = 0;
@@ -367,7 +371,8 @@ __device__ __forceinline__ void hist_crossing(Smem& sm, uint32_t base, uint32_t 
     for (int j = 0; j < PER; ++j) sum += sm.hist[hslot(base + NB - 1 - (l * PER + j))];
     const uint32_t incl = wave_scan(sum, 0u, OpAdd());
     const uint32_t excl = incl - sum;
-    auto find = [&](uint32_t r, uint32_t& d, uint32_t& a) {
+    uint32_t b2;
+    auto find = [&](uint32_t r, uint32_t& d, uint32_t& a, uint32_t& b) {
         const uint64_t m = ballot(incl >= r);
         const int L = m ? __builtin_ctzll(m) : 63;
         const uint32_t exL = (uint32_t)__builtin_amdgcn_readlane((int)excl, L);
@@ -377,13 +382,14 @@ __device__ __forceinline__ void hist_crossing(Smem& sm, uint32_t base, uint32_t 
         const int J = m2 ? __builtin_ctzll(m2) : PER - 1;
         d = NB - 1 - ((uint32_t)L * PER + (uint32_t)J);
         a = exL + (uint32_t)__builtin_amdgcn_readlane((int)(ic - c), J);
+        b = (uint32_t)__builtin_amdgcn_readlane((int)c, J);
     };
-    find(r1, d1, a1);
+    find(r1, d1, a1, b1);
     if (r2 == r1) {
         d2 = d1;
         a2 = a1;
     } else {
-        find(r2, d2, a2);
+        find(r2, d2, a2, b2);
     }
 #pragma unroll
     for (int j = 0; j < PER; ++j) sm.hist[hslot(base + NB - 1 - (l * PER + j))] = 0;
@@ -404,13 +410,20 @@ __device__ __forceinline__ void hist_crossing(Smem& sm, uint32_t base, uint32_t 
 // after a barrier wave 0 alone finds the digit holding the remaining rank and
 // zeroes the bins; a second barrier publishes the digit.  The histogram must
 // be zero on entry and is zero on exit.  Every thread must call it.
-template <class Visit>
-__device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, uint32_t lo,
-                                             uint32_t hi, int min_bit, uint32_t& kth,
-                                             uint32_t& n_greater) {
+// RANGE: the passes may also end early, once the digit holding the remaining
+// rank holds exactly that many keys: every key of it then belongs to the top
+// r, whatever its unresolved low bits.  kth_top receives the largest key the
+// resolved digits allow (kth with every unresolved bit set), so the top r is
+// the n_greater keys above kth_top and the r - n_greater keys in
+// [kth, kth_top]; without an early end, kth_top = kth | (bits below min_bit).
+template <bool RANGE, class Visit>
+__device__ __forceinline__ void block_select_bits(Smem& sm, Visit visit, uint32_t r, uint32_t lo,
+                                                  uint32_t hi, int min_bit, uint32_t& kth,
+                                                  uint32_t& kth_top, uint32_t& n_greater) {
     const uint32_t low_mask = min_bit >= 32 ? 0xFFFFFFFFu : ((1u << min_bit) - 1u);
     if (((lo ^ hi) & ~low_mask) == 0) {  // all keys share the bits that matter
         kth = lo & ~low_mask;
+        kth_top = kth | low_mask;
         n_greater = 0;
         // (uniform branch) the barrier that a pass would end with: lo and hi
         // came from block_minmax, whose per-wave slots the next one rewrites
@@ -431,11 +444,12 @@ __device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, 
         });
         lds_sync();
         if (threadIdx.x < 64) {
-            uint32_t d, a, d2, a2;
-            hist_crossing<NBINS / 64>(sm, 0u, krem, krem, d, a, d2, a2);
+            uint32_t d, a, d2, a2, b;
+            hist_crossing<NBINS / 64>(sm, 0u, krem, krem, d, a, d2, a2, b);
             if (threadIdx.x == 0) {
                 sm.sel_digit = d;
                 sm.sel_above = a;
+                sm.sel_digit2 = b;  // (a free word here) the digit's own count
             }
         }
         lds_sync();
@@ -444,9 +458,21 @@ __device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, 
         krem -= above;
         prefix |= d << shift;
         mask |= dmask << shift;
+        if constexpr (RANGE) {
+            if (sm.sel_digit2 == krem) break;  // (uniform) the whole digit completes the rank
+        }
     }
     kth = prefix;
+    kth_top = prefix | ~mask;
     n_greater = gt;
+}
+
+template <class Visit>
+__device__ __forceinline__ void block_select(Smem& sm, Visit visit, uint32_t r, uint32_t lo,
+                                             uint32_t hi, int min_bit, uint32_t& kth,
+                                             uint32_t& n_greater) {
+    uint32_t top;
+    block_select_bits<false>(sm, visit, r, lo, hi, min_bit, kth, top, n_greater);
 }
 
 // Two lower bounds at once: the r1-th and r2-th largest keys of the set that
@@ -479,7 +505,8 @@ __device__ __forceinline__ void block_select_pair(Smem& sm, Visit visit, uint32_
     lds_sync();
     if (threadIdx.x < 64) {
         uint32_t d1, a1, d2, a2;
-        hist_crossing<NBINS / 64>(sm, 0u, r1, r2, d1, a1, d2, a2);
+        uint32_t b1;
+        hist_crossing<NBINS / 64>(sm, 0u, r1, r2, d1, a1, d2, a2, b1);
         if (threadIdx.x == 0) {
             sm.sel_digit = d1;
             sm.sel_above = a1;
@@ -500,10 +527,10 @@ __device__ __forceinline__ void block_select_pair(Smem& sm, Visit visit, uint32_
     if (threadIdx.x < 64) {
         constexpr int PER = (1 << W2) / 64 > 0 ? (1 << W2) / 64 : 1;
         // with W2 < 6 the 64-lane view covers 64 bins; the digits above 2^W2 are zero
-        uint32_t e1, b1, e2, b2, x, y;
-        hist_crossing<PER>(sm, 0u, q1, base2 ? q1 : q2, e1, b1, x, y);
+        uint32_t e1, b1, e2, b2, x, y, z;
+        hist_crossing<PER>(sm, 0u, q1, base2 ? q1 : q2, e1, b1, x, y, z);
         if (base2) {
-            hist_crossing<PER>(sm, base2, q2, q2, e2, b2, x, y);
+            hist_crossing<PER>(sm, base2, q2, q2, e2, b2, x, y, z);
         } else {
             e2 = x;
         }
@@ -528,6 +555,21 @@ __device__ __forceinline__ void block_select_exact(Smem& sm, Visit visit, uint32
     });
     block_minmax(sm, lo, hi);
     block_select(sm, visit, r, lo, hi, 0, kth, n_greater);
+}
+
+// The same, allowed to end early: the top r are the n_greater keys above
+// kth_top and the r - n_greater keys in [kth, kth_top] (block_select_bits).
+template <class Visit>
+__device__ __forceinline__ void block_select_range(Smem& sm, Visit visit, uint32_t r,
+                                                   uint32_t& kth, uint32_t& kth_top,
+                                                   uint32_t& n_greater) {
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    visit([&](uint32_t key) {
+        lo = key < lo ? key : lo;
+        hi = key > hi ? key : hi;
+    });
+    block_minmax(sm, lo, hi);
+    block_select_bits<true>(sm, visit, r, lo, hi, 0, kth, kth_top, n_greater);
 }
 
 }  // namespace vts

@@ -94,9 +94,13 @@ struct Params {
     int32_t helpers;     // balanced placement of 2 * BALANCE_CUS rows: long rows get a second unit
     int32_t split_cols;  // (helpers) the shortest window that may be split
 #ifdef VTS_PHASE_STAMPS
-    uint64_t* stamps;  // phase-timing build: 8 stamps per unit, or null
+    uint64_t* stamps;  // phase-timing build: VTS_STAMPS_PER_UNIT stamps per unit, or null
 #endif
 };
+
+#ifdef VTS_PHASE_STAMPS
+constexpr int VTS_STAMPS_PER_UNIT = 16;
+#endif
 
 enum { FORCE_NONE = 0, FORCE_CAREFUL = 1, FORCE_FALLBACK = 2 };
 

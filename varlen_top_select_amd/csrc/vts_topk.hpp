@@ -46,6 +46,41 @@
 #include "vts_device.hpp"
 #include "vts_internal.h"
 
+// Phase stamps, compiled in only for the phase-timing build (-DVTS_PHASE_STAMPS,
+// varlen_top_select_amd/phases.py): thread 0 of a workgroup writes the 100 MHz
+// real-time counter when the unit starts (0), knows its window (1), has its
+// rungs (2), has streamed (3), has written its outputs (4) and has taken its
+// split-row ticket (5); slot 6 holds the hardware id (HW_ID | XCC_ID << 32)
+// and slot 7 the row and its valid length; the final selection stamps its
+// start (8) and the moment its k-th key is known (9); a split row's unit
+// stamps the start of its publication (11) and the barrier after it (12),
+// and its merging unit the moment it has read the lists' counts (10).
+#ifdef VTS_PHASE_STAMPS
+#define VTS_STAMP(i)                                                           \
+    do {                                                                       \
+        if (threadIdx.x == 0 && p.stamps)                                      \
+            gstore(p.stamps + (size_t)sm.stamp_unit * VTS_STAMPS_PER_UNIT + (i), \
+                   (uint64_t)__builtin_amdgcn_s_memrealtime());                \
+    } while (0)
+#define VTS_STAMP_ID(row, len)                                                 \
+    do {                                                                       \
+        if (threadIdx.x == 0 && p.stamps) {                                    \
+            gstore(p.stamps + (size_t)sm.stamp_unit * VTS_STAMPS_PER_UNIT + 6, \
+                   (uint64_t)__builtin_amdgcn_s_getreg(0xF804) |               \
+                       ((uint64_t)__builtin_amdgcn_s_getreg(0xF814) << 32));   \
+            gstore(p.stamps + (size_t)sm.stamp_unit * VTS_STAMPS_PER_UNIT + 7, \
+                   (uint64_t)(uint32_t)(row) | ((uint64_t)(len) << 32));       \
+        }                                                                      \
+    } while (0)
+#else
+#define VTS_STAMP(i) \
+    do {             \
+    } while (0)
+#define VTS_STAMP_ID(row, len) \
+    do {                       \
+    } while (0)
+#endif
+
 namespace vts {
 
 // ---------------------------------------------------------------------------
@@ -1563,26 +1598,48 @@ __device__ __forceinline__ void ordered_emit(Smem& sm, const Params& p, int r, i
 template <int DT, class Policy, class Src>
 __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r, int64_t base,
                                                 const typename Traits<DT>::raw_t* row, const Src& src) {
+    VTS_STAMP(8);
     uint32_t K, gt;
-    block_select_exact(
-        sm,
-        [&](auto f) {
-            src.for_each(sm, [&](bool ok, uint32_t key, uint32_t) {
-                if (ok) f(key);
-            });
-        },
-        (uint32_t)p.k, K, gt);
+    const auto keys = [&](auto f) {
+        src.for_each(sm, [&](bool ok, uint32_t key, uint32_t) {
+            if (ok) f(key);
+        });
+    };
     if constexpr (Policy::ORDERED) {
+        block_select_exact(sm, keys, (uint32_t)p.k, K, gt);
+        VTS_STAMP(9);
         ordered_emit<DT, Policy>(sm, p, r, base, row, src, K, gt);
         return;
     }
+    // The top k: the gt keys above Ktop and the k - gt first keys in [K,
+    // Ktop] (every key of that range when the selection ended on a digit
+    // that completes the rank; otherwise K == Ktop, the k-th key).  Only
+    // 32-bit keys take the early end: it saves their third pass, while
+    // 16-bit keys need two passes at most.
+    constexpr bool RANGE = Traits<DT>::BITS > 16;
+    uint32_t Ktop;
+    if constexpr (RANGE) {
+        block_select_range(sm, keys, (uint32_t)p.k, K, Ktop, gt);
+    } else {
+        block_select_exact(sm, keys, (uint32_t)p.k, K, gt);
+        Ktop = K;
+    }
+    VTS_STAMP(9);
+    const uint32_t span = Ktop - K;
+    const auto above = [&](uint32_t key) { return key > Ktop; };
+    const auto at = [&](uint32_t key) {  // key in [K, Ktop]
+        if constexpr (RANGE) return key - K <= span;
+        else return key == K;
+    };
     const uint32_t need_eq = (uint32_t)p.k - gt;
     // With a page table whose entries for the row's window fit the staging
     // area (free now that the selections are done), they go to LDS and the
     // translation reads no global memory between the output stores.  The
     // first TJ * NT entries are read here and land while the outputs are
-    // counted; the rest of a longer window are read after the count.
-    constexpr int TJ = 4;
+    // counted; the rest of a longer window are read after the count.  (Read
+    // before the selection instead, they made it slower by as much as they
+    // saved here.)
+    constexpr int TJ = 5;  // 1280 entries: a 65536-column window of 64-column pages
     [[maybe_unused]] uint32_t tl[TJ];
     uint32_t np = 0;
     [[maybe_unused]] StagedTable stg{};
@@ -1600,13 +1657,13 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         sm.cnt_b = 0;
     }
     lds_sync();
-    // Each thread counts its keys > K and == K; one bit-sliced wave prefix and
-    // one LDS ticket per wave and list give every thread its first output
-    // slots, and its keys are written in order from there.
+    // Each thread counts its keys above the range and in it; one bit-sliced
+    // wave prefix and one LDS ticket per wave and list give every thread its
+    // first output slots, and its keys are written in order from there.
     uint32_t ngt = 0, neq = 0;
     src.for_each(sm, [&](bool ok, uint32_t key, uint32_t) {
-        ngt += (ok && key > K) ? 1u : 0u;
-        neq += (ok && key == K) ? 1u : 0u;
+        ngt += (ok && above(key)) ? 1u : 0u;
+        neq += (ok && at(key)) ? 1u : 0u;
     });
     // (a wide source can give a thread more entries than wave_ticket_n counts)
     uint32_t og, oe;
@@ -1644,7 +1701,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
                 const uint32_t og0 = og, oe0 = oe;
                 int32_t tv[Src::SLOTS];
                 src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t col) {
-                    const bool isgt = ok && key > K, iseq = ok && key == K;
+                    const bool isgt = ok && above(key), iseq = ok && at(key);
                     const uint32_t pos = isgt ? og : gt + oe;
                     tv[j] = -1;
                     if (isgt || (iseq && oe < need_eq)) {
@@ -1657,7 +1714,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
                 og = og0;
                 oe = oe0;
                 src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t) {
-                    const bool isgt = ok && key > K, iseq = ok && key == K;
+                    const bool isgt = ok && above(key), iseq = ok && at(key);
                     const uint32_t pos = isgt ? og : gt + oe;
                     if (isgt || (iseq && oe < need_eq)) Policy::put_idx(p, r, pos, tv[j]);
                     og += isgt ? 1u : 0u;
@@ -1667,7 +1724,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
             if (np) {
                 // the translation reads LDS only: one pass
                 src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
-                    const bool isgt = ok && key > K, iseq = ok && key == K;
+                    const bool isgt = ok && above(key), iseq = ok && at(key);
                     const uint32_t pos = isgt ? og : gt + oe;
                     if (isgt || (iseq && oe < need_eq)) {
                         Policy::put_raw(p, r, pos, (int32_t)col);
@@ -1682,7 +1739,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
           }
         } else {
             src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
-                const bool isgt = ok && key > K, iseq = ok && key == K;
+                const bool isgt = ok && above(key), iseq = ok && at(key);
                 const uint32_t pos = isgt ? og : gt + oe;
                 if (isgt || (iseq && oe < need_eq)) {
                     Policy::put_raw(p, r, pos, (int32_t)col);
@@ -1694,7 +1751,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         }
     } else {
         src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
-            const bool isgt = ok && key > K, iseq = ok && key == K;
+            const bool isgt = ok && above(key), iseq = ok && at(key);
             const uint32_t pos = isgt ? og : gt + oe;
             if (isgt || (iseq && oe < need_eq))
                 Policy::template emit<DT>(p, r, base, pos, (int32_t)col, from_key<DT>(key));
@@ -1906,38 +1963,6 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
 // the kernel
 // ---------------------------------------------------------------------------
 
-// Phase stamps, compiled in only for the phase-timing build (-DVTS_PHASE_STAMPS,
-// varlen_top_select_amd/phases.py): thread 0 of a unit writes the 100 MHz
-// real-time counter when the unit starts (0), knows its window (1), has its
-// rungs (2), has streamed (3), has written its outputs (4) and has taken its
-// split-row ticket (5); slot 6 holds the hardware id (HW_ID | XCC_ID << 32)
-// and slot 7 the row and its valid length.
-#ifdef VTS_PHASE_STAMPS
-#define VTS_STAMP(i)                                                           \
-    do {                                                                       \
-        if (threadIdx.x == 0 && p.stamps)                                      \
-            gstore(p.stamps + (size_t)unit * 8 + (i),                          \
-                   (uint64_t)__builtin_amdgcn_s_memrealtime());                \
-    } while (0)
-#define VTS_STAMP_ID(row, len)                                                 \
-    do {                                                                       \
-        if (threadIdx.x == 0 && p.stamps) {                                    \
-            gstore(p.stamps + (size_t)unit * 8 + 6,                            \
-                   (uint64_t)__builtin_amdgcn_s_getreg(0xF804) |               \
-                       ((uint64_t)__builtin_amdgcn_s_getreg(0xF814) << 32));   \
-            gstore(p.stamps + (size_t)unit * 8 + 7,                            \
-                   (uint64_t)(uint32_t)(row) | ((uint64_t)(len) << 32));       \
-        }                                                                      \
-    } while (0)
-#else
-#define VTS_STAMP(i) \
-    do {             \
-    } while (0)
-#define VTS_STAMP_ID(row, len) \
-    do {                       \
-    } while (0)
-#endif
-
 // WIDE: the instantiation for top_k > 2048 (unordered policies only), whose
 // candidate lists outgrow the registers; see the WIDE branch below.  HINT:
 // the instantiation for calls with a hint (varlen, top_k <= 2048), whose
@@ -1946,6 +1971,11 @@ template <int DT, class Policy, bool WIDE, bool HINT>
 __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bid, uint32_t unit) {
     using raw_t = typename Traits<DT>::raw_t;
     constexpr bool ORD = Policy::ORDERED;  // deterministic mode: canonical keys
+#ifdef VTS_PHASE_STAMPS
+    // the workgroup's slot (thread 0 alone writes and reads it), kept when a
+    // split row renumbers the unit
+    if (threadIdx.x == 0) sm.stamp_unit = unit;
+#endif
     VTS_STAMP(0);
     // The row and its window are the same in every lane, but they arrive
     // through LDS and vector loads; readfirstlane puts them in scalar
@@ -2234,6 +2264,7 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     }
 
     // split row: publish this unit's on-chip candidates, then take a ticket
+    VTS_STAMP(11);
     for (uint32_t q = threadIdx.x; q < own; q += NT) {
         gstore(gkey + q, sm.key[q]);
         gstore(gidx + q, sm.idx[q]);
@@ -2250,6 +2281,7 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     // before the barrier that releases its other threads to read.  One fence
     // per workgroup: each one writes back or invalidates the whole L2.
     __syncthreads();
+    VTS_STAMP(12);
     if (threadIdx.x == 0) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const uint32_t old = __hip_atomic_fetch_add((VTS_GLOBAL uint32_t*)(p.ws_ticket + r), 1u,
@@ -2264,12 +2296,40 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
 
     // last unit of the row: merge
     const uint32_t unit0 = (uint32_t)r * (uint32_t)p.nsplit;
+    const uint32_t* rkey = p.ws_key + (size_t)unit0 * (uint32_t)p.ws_slots;
+    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * (uint32_t)p.ws_slots;
+    // With at most GL lists, the first GL_SLOTS entries of every list (of
+    // this unit's own list: its spilled entries from slot own on) are read
+    // now, before their counts are known, so that the lists and the counts
+    // arrive in one round trip; entries past a list's count are dropped
+    // below.  Register e holds entry (e % GPL) * NT + thread of list e / GPL.
+    // 32-bit keys only: measured on the 16-bit kernels (two lists per split
+    // row there), the read-ahead cost more than the round trip it saves.
+    constexpr int GL = 4, GPL = 4, GS = GL * GPL;
+    constexpr uint32_t GL_SLOTS = (uint32_t)(GPL * NT);
+    static_assert(GL_SLOTS <= (uint32_t)HI_SLOTS, "read-ahead within a unit's workspace slots");
+    const bool ahead = Traits<DT>::BITS > 16 && eff <= GL && (uint32_t)p.ws_slots >= own + GL_SLOTS;
+    uint32_t gk[GS], gi[GS];
+    if (ahead) {
+#pragma unroll
+        for (int e = 0; e < GS; ++e) {
+            const int q = e / GPL;
+            const uint32_t j = (uint32_t)(e % GPL) * NT + threadIdx.x + (q == c ? own : 0u);
+            gk[e] = 0u;
+            gi[e] = 0u;
+            if (q < eff && (q != c || j < nh)) {
+                gk[e] = gload(rkey + (size_t)q * (uint32_t)p.ws_slots + j);
+                gi[e] = gload(ridx + (size_t)q * (uint32_t)p.ws_slots + j);
+            }
+        }
+    }
     if (threadIdx.x < (unsigned)eff) {
         sm.seg_hi[threadIdx.x] = gload(p.ws_count + unit0 + threadIdx.x);
         sm.seg_lo[threadIdx.x] = gload(p.ws_count_up + unit0 + threadIdx.x);
     }
     if (threadIdx.x == 0) gstore(p.ws_ticket + r, 0u);  // self-restoring
     __syncthreads();
+    VTS_STAMP(10);
     uint32_t th = 0, tup = 0;
     bool mixed = false;  // some unit was re-filtered
     for (int q = 0; q < eff; ++q) {
@@ -2285,8 +2345,6 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
         return;
     }
     const bool rupper = !mixed && tup >= (uint32_t)p.k;
-    const uint32_t* rkey = p.ws_key + (size_t)unit0 * (uint32_t)p.ws_slots;
-    const uint32_t* ridx = p.ws_idx + (size_t)unit0 * (uint32_t)p.ws_slots;
     if (threadIdx.x == 0) {
         if (th > (uint32_t)CAP) gatomic_add(p.ws_stats + 2, 1u);
         if (!rupper) gatomic_add(p.ws_stats + 3, 1u);
@@ -2299,6 +2357,34 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
         // the row is selected directly.  seg_lo now holds each list's first
         // gathered slot.
         const uint32_t m = th - own;
+        // the read-ahead holds every list whole: place its entries behind
+        // this unit's on-chip ones, list after list
+        uint32_t gcount[GL], gbase[GL];
+        bool whole = ahead;
+        uint32_t acc = own;
+#pragma unroll
+        for (int q = 0; q < GL; ++q) {
+            gcount[q] = 0u;
+            if (q < eff) gcount[q] = sm.seg_hi[q] - (q == c ? own : 0u);
+            gbase[q] = acc;
+            acc += gcount[q];
+            whole = whole && gcount[q] <= GL_SLOTS;
+        }
+        if (whole) {
+#pragma unroll
+            for (int e = 0; e < GS; ++e) {
+                const int q = e / GPL;
+                const uint32_t j = (uint32_t)(e % GPL) * NT + threadIdx.x;
+                if (q < eff && j < gcount[q]) {
+                    sm.key[gbase[q] + j] = gk[e];
+                    sm.idx[gbase[q] + j] = gi[e];
+                }
+            }
+            __syncthreads();
+            select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, th, rupper ? G.T2 : 0u));
+            VTS_STAMP(4);
+            return;
+        }
         __syncthreads();  // every thread has read the counts in seg_lo
         if (threadIdx.x == 0) {
             uint32_t acc = 0;
