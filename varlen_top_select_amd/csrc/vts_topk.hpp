@@ -54,7 +54,9 @@
 // and slot 7 the row and its valid length; the final selection stamps its
 // start (8) and the moment its k-th key is known (9); a split row's unit
 // stamps the start of its publication (11) and the barrier after it (12),
-// and its merging unit the moment it has read the lists' counts (10).
+// and its merging unit the moment it has read the lists' counts (10); the
+// emission stamps its output tickets (13) and, with a page table, the staged
+// table (14).
 #ifdef VTS_PHASE_STAMPS
 #define VTS_STAMP(i)                                                           \
     do {                                                                       \
@@ -95,6 +97,18 @@ struct StagedTable {
     uint32_t jlo, jhi, sh;
 };
 
+// The outputs of one row as buffer resources over the row's k slots of each
+// output array; an array that was not asked for gets an empty resource,
+// whose stores the range check drops.  A slot's stores then need only its
+// byte offset: no 64-bit address, no test of the array.
+struct OutRow {
+    __amdgpu_buffer_rsrc_t a, b;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t out_rsrc(void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, (int)bytes, 0x00020000);
+}
+
 struct VarlenPolicy {
     // the output needs no memory reads of its own
     static constexpr bool GATHERS = false;
@@ -132,6 +146,24 @@ struct VarlenPolicy {
             using raw_t = typename Traits<DT>::raw_t;
             gstore(static_cast<raw_t*>(p.out_vals) + o, (raw_t)raw);
         }
+    }
+    // row r's outputs: a = indices, b = values
+    template <int DT>
+    __device__ __forceinline__ static OutRow out_row(const Params& p, int r) {
+        using raw_t = typename Traits<DT>::raw_t;
+        const int64_t o = (int64_t)r * p.k;
+        const uint32_t k = (uint32_t)p.k;
+        return OutRow{out_rsrc(p.out_idx + o, k * 4u),
+                      p.out_vals ? out_rsrc(static_cast<raw_t*>(p.out_vals) + o, k * (uint32_t)sizeof(raw_t))
+                                 : out_rsrc(p.out_idx, 0u)};
+    }
+    template <int DT>
+    __device__ __forceinline__ static void put(const OutRow& o, uint32_t pos, int32_t col, uint32_t raw) {
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)col, o.a, (int)(pos * 4u), 0, 0);
+        if constexpr (Traits<DT>::BITS == 32)
+            __builtin_amdgcn_raw_buffer_store_b32(raw, o.b, (int)(pos * 4u), 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b16((unsigned short)raw, o.b, (int)(pos * 2u), 0, 0);
     }
 };
 
@@ -237,12 +269,14 @@ struct PagePolicy {
         }
     }
     // translate from the staged entries (the same bits: the low 32 bits of
-    // page * P + col % P)
-    __device__ __forceinline__ static int32_t translate_staged(const StagedTable& t, int32_t col) {
-        if (col < 0) return -1;
-        const uint32_t j = (uint32_t)col >> t.sh;
-        if (j < t.jlo || j >= t.jhi) return -1;
-        return (int32_t)((t.table[j] << t.sh) + ((uint32_t)col & ((1u << t.sh) - 1u)));
+    // page * P + col % P), for any 32-bit column and without a branch: a
+    // column outside the staged range reads entry 0 (always staged) and
+    // yields -1
+    __device__ __forceinline__ static int32_t translate_staged(const StagedTable& t, uint32_t col) {
+        const uint32_t j = col >> t.sh;
+        const bool in = (int32_t)col >= 0 && j >= t.jlo && j < t.jhi;
+        const uint32_t e = t.table[in ? j : 0u];
+        return in ? (int32_t)((e << t.sh) + (col & ((1u << t.sh) - 1u))) : -1;
     }
     // output slot pos: the raw index col, and the translated index t
     __device__ __forceinline__ static void put_raw(const Params& p, int r, uint32_t pos, int32_t col) {
@@ -250,6 +284,20 @@ struct PagePolicy {
     }
     __device__ __forceinline__ static void put_idx(const Params& p, int r, uint32_t pos, int32_t t) {
         gstore(p.out_idx + (int64_t)r * p.k + pos, t);
+    }
+    // row r's outputs: a = translated indices, b = raw indices
+    template <int DT>
+    __device__ __forceinline__ static OutRow out_row(const Params& p, int r) {
+        const int64_t o = (int64_t)r * p.k;
+        const uint32_t k = (uint32_t)p.k;
+        return OutRow{out_rsrc(p.out_idx + o, k * 4u),
+                      p.out_raw ? out_rsrc(p.out_raw + o, k * 4u) : out_rsrc(p.out_idx, 0u)};
+    }
+    __device__ __forceinline__ static void put_raw(const OutRow& o, uint32_t pos, int32_t col) {
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)col, o.b, (int)(pos * 4u), 0, 0);
+    }
+    __device__ __forceinline__ static void put_idx(const OutRow& o, uint32_t pos, int32_t t) {
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)t, o.a, (int)(pos * 4u), 0, 0);
     }
 };
 
@@ -1674,6 +1722,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
         og = wave_ticket_any(&sm.cnt_a, ngt);
         oe = wave_ticket_any(&sm.cnt_b, neq);
     }
+    VTS_STAMP(13);
     if constexpr (Policy::GATHERS) {
         const auto w = Policy::row(p, r, base);
         // (sources held in registers only; a wide source translates inline)
@@ -1689,6 +1738,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
                 sm.table[j] = j >= stg.jlo && j < stg.jhi ? (uint32_t)gload(p.pt + (int64_t)r * p.pt_stride + w.start + j) : 0u;
             lds_sync();
         }
+        VTS_STAMP(14);
         if (ahead) {
           if constexpr (Src::SLOTS > 0) {
             // Every table read of the thread is issued before its first output
@@ -1697,6 +1747,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
             // share one completion counter), one memory round trip per register.
             // The first pass also writes the raw indices, so the registers that
             // held them take the translated ones and the pass adds none.
+            const OutRow o = Policy::template out_row<DT>(p, r);
             auto two_passes = [&](auto translate) {
                 const uint32_t og0 = og, oe0 = oe;
                 int32_t tv[Src::SLOTS];
@@ -1705,7 +1756,7 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
                     const uint32_t pos = isgt ? og : gt + oe;
                     tv[j] = -1;
                     if (isgt || (iseq && oe < need_eq)) {
-                        Policy::put_raw(p, r, pos, (int32_t)col);
+                        Policy::put_raw(o, pos, (int32_t)col);
                         tv[j] = translate((int32_t)col);
                     }
                     og += isgt ? 1u : 0u;
@@ -1716,19 +1767,26 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
                 src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t) {
                     const bool isgt = ok && above(key), iseq = ok && at(key);
                     const uint32_t pos = isgt ? og : gt + oe;
-                    if (isgt || (iseq && oe < need_eq)) Policy::put_idx(p, r, pos, tv[j]);
+                    if (isgt || (iseq && oe < need_eq)) Policy::put_idx(o, pos, tv[j]);
                     og += isgt ? 1u : 0u;
                     oe += iseq ? 1u : 0u;
                 });
             };
             if (np) {
-                // the translation reads LDS only: one pass
-                src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
+                // The translation reads LDS only.  Every register's entry is
+                // read first, without a branch (a read inside each store's
+                // condition would wait for its own round trip), then the
+                // stores.
+                int32_t tv[Src::SLOTS];
+                src.for_each_slot([&](int j, bool, uint32_t, uint32_t col) {
+                    tv[j] = Policy::translate_staged(stg, col);
+                });
+                src.for_each_slot([&](int j, bool ok, uint32_t key, uint32_t col) {
                     const bool isgt = ok && above(key), iseq = ok && at(key);
                     const uint32_t pos = isgt ? og : gt + oe;
                     if (isgt || (iseq && oe < need_eq)) {
-                        Policy::put_raw(p, r, pos, (int32_t)col);
-                        Policy::put_idx(p, r, pos, Policy::translate_staged(stg, (int32_t)col));
+                        Policy::put_raw(o, pos, (int32_t)col);
+                        Policy::put_idx(o, pos, tv[j]);
                     }
                     og += isgt ? 1u : 0u;
                     oe += iseq ? 1u : 0u;
@@ -1738,23 +1796,25 @@ __device__ __forceinline__ void select_and_emit(Smem& sm, const Params& p, int r
             }
           }
         } else {
+            const OutRow o = Policy::template out_row<DT>(p, r);
             src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
                 const bool isgt = ok && above(key), iseq = ok && at(key);
                 const uint32_t pos = isgt ? og : gt + oe;
                 if (isgt || (iseq && oe < need_eq)) {
-                    Policy::put_raw(p, r, pos, (int32_t)col);
-                    Policy::put_idx(p, r, pos, Policy::translate(p, r, w, (int32_t)col));
+                    Policy::put_raw(o, pos, (int32_t)col);
+                    Policy::put_idx(o, pos, Policy::translate(p, r, w, (int32_t)col));
                 }
                 og += isgt ? 1u : 0u;
                 oe += iseq ? 1u : 0u;
             });
         }
     } else {
+        const OutRow o = Policy::template out_row<DT>(p, r);
         src.for_each(sm, [&](bool ok, uint32_t key, uint32_t col) {
             const bool isgt = ok && above(key), iseq = ok && at(key);
             const uint32_t pos = isgt ? og : gt + oe;
             if (isgt || (iseq && oe < need_eq))
-                Policy::template emit<DT>(p, r, base, pos, (int32_t)col, from_key<DT>(key));
+                Policy::template put<DT>(o, pos, (int32_t)col, from_key<DT>(key));
             og += isgt ? 1u : 0u;
             oe += iseq ? 1u : 0u;
         });

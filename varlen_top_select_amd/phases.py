@@ -63,7 +63,7 @@ def report(name: str, st: np.ndarray, event_us: float) -> None:
     st = st[st[:, 0] > 0]
     t0 = st[:, 0].min()
     us = lambda i: np.where(st[:, i] > 0, (st[:, i] - t0) / 100.0, np.nan)  # 100 MHz ticks
-    s = {i: us(i) for i in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12)}
+    s = {i: us(i) for i in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 14)}
     n = (st[:, 7] >> 32).astype(np.int64)
     print(f"== {name}: {st.shape[0]} units, kernel time by events {event_us:.1f} us")
     print("  unit start            ", _pct(s[0]))
@@ -79,6 +79,9 @@ def report(name: str, st: np.ndarray, event_us: float) -> None:
     print("    counts -> select    ", _pct(s[8] - s[10]))
     print("    select -> k-th key  ", _pct(s[9] - s[8]))
     print("    k-th key -> written ", _pct(s[4] - s[9]))
+    print("      k-th -> tickets   ", _pct(s[13] - s[9]))
+    print("      tickets -> table  ", _pct(s[14] - s[13]))
+    print("      table -> written  ", _pct(s[4] - s[14]))
     print("  rungs ready at        ", _pct(s[2]))
     print("  stream end at         ", _pct(s[3]))
     print("  ticket at             ", _pct(s[5]))
