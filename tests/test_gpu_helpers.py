@@ -1,11 +1,12 @@
-"""GPU parity of the second workgroups that the length-balanced placement of
-512 rows gives to rows far longer than the batch's mean (at least 256 KB of
-window and more than twice the mean; only the 128 longest rows can take one).
+"""GPU parity of the length-balanced units of 512-row batches: the launch has
+1024 workgroups, and every row is cut into e = min(8, ceil(n / U)) units,
+where U is about the batch's columns per compute unit and at least 96 KB.
 
-Two length profiles: "few" -- a handful of long rows around the 256 KB bound
-(one element short of it, exactly on it, one past it) among short rows -- and
-"many" -- 200 long rows, so that rows of rank 128 and beyond qualify by length
-but must stay whole.  Every case prints its name before its GPU step.
+Three length profiles: "few" -- a handful of long rows (e up to 8) among
+short ones, with lengths one element around a unit bound; "many" -- 200 long
+rows, so that U is large and they split in two; "spread" -- log-uniform
+lengths, every unit count from 1 to the maximum.  Every case prints its name
+before its GPU step.
 """
 import numpy as np
 import pytest
@@ -22,23 +23,25 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 R = 512
-W = 196608  # at least 256 KB of fp32, fp16 and bf16 columns
+W = 196608  # 768 KB of fp32, 384 KB of 16-bit columns
 
 
 def _split_cols(dtype):
-    return (256 * 1024) // (4 if dtype == F32 else 2)
+    return (96 * 1024) // (4 if dtype == F32 else 2)
 
 
 def _lengths(profile, dtype, rng):
     n = rng.integers(100, 3001, size=R).astype(np.int64)
     s = _split_cols(dtype)
     if profile == "few":
-        special = [W, s, s - 1, s + 1, (s + W) // 2, W - 7, 2 * s if 2 * s <= W else W - 1]
+        special = [W, s, s - 1, s + 1, 2 * s, 2 * s + 1, 3 * s - 1, (s + W) // 2, W - 7]
         at = rng.choice(R, size=len(special), replace=False)
         n[at] = special
-    else:
+    elif profile == "many":
         at = rng.choice(R, size=200, replace=False)
         n[at] = W - rng.integers(0, 64, size=200)
+    else:
+        n = np.exp(rng.uniform(np.log(100), np.log(W), size=R)).astype(np.int64)
     return n
 
 
@@ -57,25 +60,29 @@ def _varlen(profile, dtype, k, seed):
                     pre_idx=None, return_values=True)
 
 
-def _expected_splits(wl):
+def _expected_units(wl):
+    """(split rows, most units of a row, units in all) under the placement's
+    rule: U = max(96 KB, min(width, 4 * sum(n >> 10) + 4 * R)) columns."""
     n = np.minimum(wl.seq_lens.astype(np.int64), W)
-    mean2 = 2 * int((n >> 10).sum())
-    qual = (n >= _split_cols(wl.dtype)) & ((n >> 10) * R >= mean2)
-    order = np.argsort(-n, kind="stable")
-    return int(qual[order[:128]].sum()), int(qual.sum())
+    U = max(_split_cols(wl.dtype), min(W, 4 * int((n >> 10).sum()) + 4 * R))
+    e = np.clip(-(-n // U), 1, 8)
+    return int((e > 1).sum()), int(e.max()), int(e.sum())
+
+
+PROFILES = ["few", "many", "spread"]
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16, F16])
-@pytest.mark.parametrize("profile", ["few", "many"])
+@pytest.mark.parametrize("profile", PROFILES)
 def test_helpers_varlen(profile, dtype):
-    wl = _varlen(profile, dtype, 2048, 700 + dtype + (10 if profile == "many" else 0))
-    split, qual = _expected_splits(wl)
-    say(f"helpers varlen {profile} dtype {dtype}: {split} rows split, {qual} qualify")
-    assert split > 0
+    wl = _varlen(profile, dtype, 2048, 700 + dtype + 10 * PROFILES.index(profile))
+    split, most, units = _expected_units(wl)
+    say(f"units varlen {profile} dtype {dtype}: {split} rows split, up to {most} units, {units} in all")
+    assert split > 0 and units <= 2 * R
     idx, vals, _ = run_varlen(wl)
     errs = check_varlen(wl, idx, vals)
     assert errs == [], "\n".join(errs[:8])
-    say("the same without the balanced placement (no second workgroups)")
+    say("the same without the balanced placement (one unit per row)")
     with tuning(no_balance=1):
         idx2, vals2, _ = run_varlen(wl)
     errs = check_varlen(wl, idx2, vals2)
@@ -83,10 +90,10 @@ def test_helpers_varlen(profile, dtype):
 
 
 @pytest.mark.parametrize("dtype", [F32, BF16])
-@pytest.mark.parametrize("profile", ["few", "many"])
+@pytest.mark.parametrize("profile", PROFILES)
 def test_helpers_ordered(profile, dtype):
-    wl = _varlen(profile, dtype, 1024, 800 + dtype + (10 if profile == "many" else 0))
-    say(f"helpers ordered (SMALL) {profile} dtype {dtype}")
+    wl = _varlen(profile, dtype, 1024, 800 + dtype + 10 * PROFILES.index(profile))
+    say(f"units ordered (SMALL) {profile} dtype {dtype}")
     idx, vals, _ = run_varlen(wl, tie="small")
     ref_idx, ref_vals, _ = oracle.topk_varlen_ordered(wl.x[:, :W], wl.dtype, wl.seq_lens, wl.k,
                                                       "small", return_values=True)
@@ -97,7 +104,7 @@ def test_helpers_ordered(profile, dtype):
 
 def test_helpers_wide():
     wl = _varlen("few", BF16, 4096, 901)
-    say("helpers varlen top_k 4096 (wide kernels), bf16")
+    say("units varlen top_k 4096 (wide kernels), bf16")
     idx, vals, _ = run_varlen(wl)
     errs = check_varlen(wl, idx, vals)
     assert errs == [], "\n".join(errs[:8])
@@ -116,7 +123,7 @@ def test_helpers_page_transform():
     wl.page_size = 64
     wl.page_table = rng.permutation(R * P).astype(np.int32).reshape(R, P)
     wl.page_table_row_starts = rng.integers(0, 16, size=R).astype(np.int32)
-    say("helpers page transform, fp16, page 64")
+    say("units page transform, fp16, page 64")
     out, raw, _ = run_transform(wl)
     errs = check_transform_wl(wl, out, raw)
     assert errs == [], "\n".join(errs[:8])

@@ -51,18 +51,17 @@ uint64_t* g_stamps = nullptr;  // phase-timing build: where the next launches st
 size_t itemsize(int32_t dtype) { return dtype == VTS_F32 ? 4 : 2; }
 
 // With the length-balanced placement of 2 * BALANCE_CUS rows (two per compute
-// unit), the rows far longer than the batch's mean (more than twice it, and
-// at least LONG_ROW_BYTES) take a second workgroup on a compute unit of their
-// own: one workgroup's stream is capped by the memory requests its compute
-// unit keeps in flight (~20 GB/s), so such a row would otherwise finish long
-// after the rest.  A split pays a second sample and a merge (~8 us), which a
-// stream of 256 KB or more at that rate outweighs (measured on DSv4 MTP:
-// 34.6 against 41.5 us cold; splitting rows of 192 or 128 KB, or every row
-// above 64 KB in four, was slower).  The rows are known only on the device,
-// which decides per row; the plan reserves the workgroups and workspace.
-constexpr int64_t LONG_ROW_BYTES = 256 * 1024;
+// unit), the launch has twice as many workgroups and every row is cut into
+// units of about the batch's columns per compute unit (placed_unit in the
+// kernel): one workgroup's stream is capped by the memory requests its
+// compute unit keeps in flight (~20 GB/s), so a row far longer than the mean
+// would otherwise finish long after the rest.  A unit is at least
+// MIN_UNIT_BYTES long: a split pays a sample per unit and a merge.  The rows
+// are known only on the device, which decides per row; the plan reserves the
+// workgroups and the workspace.
+constexpr int64_t MIN_UNIT_BYTES = 96 * 1024;
 
-int32_t split_cols(int32_t dtype) { return (int32_t)(LONG_ROW_BYTES / (int64_t)itemsize(dtype)); }
+int32_t split_cols(int32_t dtype) { return (int32_t)(MIN_UNIT_BYTES / (int64_t)itemsize(dtype)); }
 
 bool helpers_apply(int64_t num_rows, int64_t width, int32_t dtype) {
     return num_rows == 2 * BALANCE_CUS && width >= split_cols(dtype) && g_tune.no_balance == 0;
@@ -187,7 +186,7 @@ int32_t scratch_slots(int64_t num_rows, int64_t width, int32_t top_k, int32_t dt
 // unit in the workspace (>= CAP whenever a row is split: a split row's units
 // publish their on-chip lists there).
 // `cus`: the device's compute units.  The length-balanced placement (and its
-// second workgroups) assumes the dispatch order of 8 XCDs of 32 compute units
+// units) assumes the dispatch order of 8 XCDs of 32 compute units
 // (BALANCE_CUS); on any other device the rows run in order, one unit each
 // where the plan reserved two (the workspace, sized from the shape alone, is
 // then larger than needed).
@@ -253,7 +252,7 @@ void log_plan(const char* entry, const Params& p, int32_t dtype, int64_t width, 
             "placement %s | order %d | workspace slots %d per unit | device CUs %d\n",
             entry, p.num_rows, (long long)width, p.k, dtype >= 0 && dtype < 3 ? dts[dtype] : "?",
             kind, p.num_units, p.nsplit,
-            p.helpers ? ", the second only for rows far longer than the mean" : "",
+            p.helpers ? ", rows cut into length-balanced units" : "",
             p.balance ? "length-balanced" : "in row order", p.order, p.ws_slots, cus);
 }
 

@@ -34,9 +34,6 @@ inline int32_t slots_for_k(int32_t k) {
 constexpr int BALANCE_XCDS = 8;
 constexpr int BALANCE_CUS_PER_XCD = 32;
 constexpr int BALANCE_CUS = BALANCE_XCDS * BALANCE_CUS_PER_XCD;
-// With the balanced placement of 2 * BALANCE_CUS rows, the rows of the first
-// HELPER_RANKS ranks (the longest) may take a second workgroup.
-constexpr int HELPER_RANKS = 128;
 
 // Output order: any (fastest), or the deterministic mode: the ties at the
 // k-th value taken at the smallest (ORDER_SMALL) or largest (ORDER_LARGE)
@@ -91,8 +88,8 @@ struct Params {
     uint32_t* ws_key;
     uint32_t* ws_idx;
     int32_t order;  // ORDER_ANY, or ORDER_SMALL / ORDER_LARGE (+ ORDER_NOSORT)
-    int32_t helpers;     // balanced placement of 2 * BALANCE_CUS rows: long rows get a second unit
-    int32_t split_cols;  // (helpers) the shortest window that may be split
+    int32_t helpers;     // balanced placement of 2 * BALANCE_CUS rows cut into length-balanced units
+    int32_t split_cols;  // (helpers) the shortest unit, in columns
 #ifdef VTS_PHASE_STAMPS
     uint64_t* stamps;  // phase-timing build: VTS_STAMPS_PER_UNIT stamps per unit, or null
 #endif

@@ -1878,10 +1878,8 @@ __device__ __forceinline__ void whole_row(Smem& sm, const Params& p, int r, int6
 // same number of columns and no unit is left with only long rows.  Every
 // workgroup derives the same ranking from the row lengths, and the map from
 // blocks to ranks is a bijection, so each row is taken exactly once; the
-// placement only changes speed.  The row's window comes back in base / n, the
-// workgroup's unit of the row in c (0; 1 for a second workgroup of a split
-// row; -1: nothing to do) and the row's unit count in eff (see below).
-// Every thread must call it.
+// placement only changes speed.  The row's window comes back in base / n;
+// c = 0 and eff = 1 (one unit per row).  Every thread must call it.
 template <class Policy>
 __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t bid,
                                             int64_t& base, int64_t& n, int& c, int& eff) {
@@ -1899,72 +1897,35 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     for (int i = 0; i < MAXPER; ++i)
         raw[i] = Policy::fetch(p, i < per ? (int)threadIdx.x + i * NT : 0);
     const float scale = (float)NB / (float)(p.width + 1);
-    uint32_t ksum = 0;  // this thread's rows: valid columns / 1024, summed (exact)
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i) {
         int64_t b, n;
         Policy::finish(p, (int)threadIdx.x + i * NT, raw[i], b, n);
         wb[i] = (uint32_t)b;
         wn[i] = (uint32_t)n;
-        ksum += i < per ? wn[i] >> 10 : 0u;
         uint32_t q = (uint32_t)((float)n * scale);  // 0..NB-1, longer rows higher
         q = q > NB - 1 ? NB - 1 : q;
         bk[i] = i < per ? NB - 1 - q : (uint32_t)NB;  // 0: longest; NB: no row
     }
-    uint32_t* ktot = sm.hist + NB;  // sum of every row's valid columns / 1024
     if (threadIdx.x < NB) cnt[threadIdx.x] = 0;
-    if (threadIdx.x == 0) {
-        sm.total = 0xFFFFFFFFu;
-        *ktot = 0;
-    }
+    if (threadIdx.x == 0) sm.total = 0xFFFFFFFFu;
     lds_sync();
 #pragma unroll
     for (int i = 0; i < MAXPER; ++i)
         if (i < per) atomicAdd(&cnt[bk[i]], 1u);
-    {
-        const uint32_t wk = wave_scan(ksum, 0u, OpAdd());  // (< 2^31: width < 2^31, R <= 1024)
-        if (lane_id() == 63) atomicAdd(ktot, wk);
-    }
     lds_sync();
-    // Workgroup bid < R lands on compute unit k % 32 of XCD x (bid = 8k + x),
-    // numbered g = 32 x + k % 32 -- or, with helpers, g = 8 (k % 32) + x, so
-    // that consecutive numbers alternate over the XCDs and the longest rows
-    // spread over all of them (measured: the contiguous numbering is 2 us
-    // faster on 1024 rows, the alternating one 3 us faster on DSv4 MTP with
-    // helpers) -- and in round j = k / 32 it takes the row of rank j * 256 + g
-    // (even rounds) or j * 256 + 255 - g (odd rounds; rank 0: the longest), a
-    // serpentine that gives every compute unit a long row and a short one.
-    // With helpers (R = 2 * BALANCE_CUS: two rows per compute unit, room for
-    // as many workgroups again), workgroup
-    // R + 128 + h (h < HELPER_RANKS = 128) -- which lands on compute unit
-    // g = 128 + h, on the XCD of the row of rank h, beside rows of ranks
-    // 128 + h and 383 - h -- is the second unit of the row of rank h, if that
-    // row is split; the other workgroups past R have nothing to do.  A row of
-    // rank < HELPER_RANKS is split in two when its window holds at least
-    // split_cols columns and more than twice the batch's mean: both of its
-    // workgroups decide this from the same integers.
-    static_assert(HELPER_RANKS == 128 && BALANCE_CUS == 256 && BALANCE_XCDS == 8,
-                  "helper slots R + 128 + h land on compute unit number 128 + h");
-    uint32_t rank;
+    // Workgroup bid lands on compute unit k % 32 of XCD x (bid = 8k + x),
+    // numbered g = 32 x + k % 32, and in round j = k / 32 it takes the row of
+    // rank j * 256 + g (even rounds) or j * 256 + 255 - g (odd rounds; rank 0:
+    // the longest), a serpentine that gives every compute unit a long row and
+    // a short one.
+    static_assert(BALANCE_CUS == 256 && BALANCE_XCDS == 8, "8 XCDs of 32 compute units");
     c = 0;
-    if (bid < (uint32_t)p.num_rows) {
-        const uint32_t x = bid % BALANCE_XCDS, k = bid / BALANCE_XCDS;
-        const uint32_t g = p.helpers ? (k % BALANCE_CUS_PER_XCD) * BALANCE_XCDS + x
-                                     : x * BALANCE_CUS_PER_XCD + k % BALANCE_CUS_PER_XCD;
-        const uint32_t j = k / BALANCE_CUS_PER_XCD;
-        rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
-    } else {
-        const uint32_t i = bid - (uint32_t)p.num_rows;
-        if (!p.helpers || i < (uint32_t)HELPER_RANKS || i >= 2u * HELPER_RANKS) {
-            c = -1;  // (uniform) no role
-            eff = 1;
-            base = 0;
-            n = 0;
-            return 0;
-        }
-        rank = i - (uint32_t)HELPER_RANKS;
-        c = 1;
-    }
+    eff = 1;
+    const uint32_t x = bid % BALANCE_XCDS, k = bid / BALANCE_XCDS;
+    const uint32_t g = x * BALANCE_CUS_PER_XCD + k % BALANCE_CUS_PER_XCD;
+    const uint32_t j = k / BALANCE_CUS_PER_XCD;
+    const uint32_t rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
     // bucket holding the rank and the rank within it (the same in every
     // thread): lane b scans bucket b's count, the first lane whose running
     // total passes the rank names it
@@ -2009,14 +1970,163 @@ __device__ __forceinline__ int balanced_row(Smem& sm, const Params& p, uint32_t 
     const int row = (int)sm.total;
     base = sm.win_base;
     n = sm.win_n;
-    const bool split = p.helpers && rank < (uint32_t)HELPER_RANKS && n >= p.split_cols &&
-                       (uint64_t)((uint32_t)n >> 10) * (uint64_t)p.num_rows >= 2ull * *ktot;
-    eff = split ? 2 : 1;
     lds_sync();  // sm.total and the histogram are rewritten later
     if (row >= 0 && row < p.num_rows) return row;
     const int r = (int)(bid % (uint32_t)p.num_rows);  // not reached: the map is a bijection
     Policy::window(p, r, base, n);
     return r;
+}
+
+// Length-balanced units for a batch of R = 2 * BALANCE_CUS rows, launched
+// with 2 * R workgroups (four per compute unit).  A workgroup's stream is
+// capped by the memory requests its compute unit keeps in flight, so a row
+// far longer than the others would finish long after them; here every row is
+// cut into e = min(EMAX_UNITS, ceil(n / U)) equal units, where U is about the
+// batch's columns per compute unit (and at least split_cols), and the units --
+// ranked by size, longest first, in NB buckets over [0, U], by row index
+// within a bucket, each row covering e consecutive ranks -- are dealt to the
+// compute units in serpentine rounds as in balanced_row (ranks g, 511 - g,
+// 512 + g, 1023 - g on compute unit g, numbered g = 8 (k % 32) + x for block
+// 8k + x so that consecutive ranks alternate over the XCDs).  U bounds the
+// units at R + BALANCE_CUS <= 2 R; the ranks past them have nothing to do.
+// Row r's units are numbered ubase(r) + c, c < e, where ubase(r) counts the
+// units of the rows before r: they index the workspace lists and counts, and
+// the row's ticket counts e.  Every workgroup derives the same units from
+// the same integers, so each unit is taken exactly once.  Returns the row;
+// base / n its window, c the unit (-1: nothing to do), eff = e, ubase.
+// Every thread must call it.
+constexpr int EMAX_UNITS = 8;
+
+template <class Policy>
+__device__ __forceinline__ int placed_unit(Smem& sm, const Params& p, uint32_t bid, int64_t& base,
+                                           int64_t& n, int& c, int& eff, uint32_t& ubase) {
+    constexpr int NB = 32;
+    constexpr int MAXPER = 2;  // rows per thread: R = 2 * NT
+    static_assert(2 * BALANCE_CUS == MAXPER * NT && BALANCE_CUS == 256 && BALANCE_XCDS == 8,
+                  "two rows per thread, four workgroups per compute unit");
+    static_assert(EMAX_UNITS <= MAX_SPLIT, "a row's lists fit the merge");
+    // scratch in the histogram, which is cleared before its first use
+    uint32_t* cnt = sm.hist;                          // NB bucket unit counts
+    uint32_t* ktot = sm.hist + NB;                    // every row's valid columns / 1024
+    uint32_t* wcnt = sm.hist + 2 * NB;                // per chunk, wave: units of the wanted bucket
+    uint32_t* wall = wcnt + MAXPER * WAVES;           // per chunk, wave: units of every row
+    uint32_t* found = wall + MAXPER * WAVES;          // the unit's row, window, c, e, ubase
+    static_assert(2 * NB + 2 * MAXPER * WAVES + 6 <= HIST_WORDS, "scratch fits the histogram");
+    uint32_t wb[MAXPER], wn[MAXPER], we[MAXPER], bk[MAXPER];
+    typename Policy::Raw raw[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) raw[i] = Policy::fetch(p, (int)threadIdx.x + i * NT);
+    uint32_t ksum = 0;  // this thread's rows: valid columns / 1024 (exact)
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        int64_t b, m;
+        Policy::finish(p, (int)threadIdx.x + i * NT, raw[i], b, m);
+        wb[i] = (uint32_t)b;
+        wn[i] = (uint32_t)m;
+        ksum += wn[i] >> 10;
+    }
+    if (threadIdx.x < NB) cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        *ktot = 0;
+        found[0] = 0xFFFFFFFFu;
+    }
+    lds_sync();
+    {
+        const uint32_t wk = wave_scan(ksum, 0u, OpAdd());  // < 2^31: R * width / 1024
+        if (lane_id() == 63) atomicAdd(ktot, wk);
+    }
+    lds_sync();
+    // U >= (the batch's columns) / BALANCE_CUS: the columns are at most
+    // 1024 ktot + 1023 R, so the units' sum of n / U is at most BALANCE_CUS and
+    // there are at most R + BALANCE_CUS units.  U <= width < 2^31.
+    const uint64_t u64 = 4ull * *ktot + 4ull * (uint64_t)p.num_rows;
+    uint32_t U = u64 < (uint64_t)p.width ? (uint32_t)u64 : (uint32_t)p.width;
+    U = U > (uint32_t)p.split_cols ? U : (uint32_t)p.split_cols;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        uint32_t e = (wn[i] + U - 1) / U;  // < 2^32: wn, U < 2^31
+        e = e < 1u ? 1u : (e > (uint32_t)EMAX_UNITS ? (uint32_t)EMAX_UNITS : e);
+        we[i] = e;
+        const uint32_t sz = wn[i] / e;  // a unit's columns
+        uint64_t q = (uint64_t)sz * NB / ((uint64_t)U + 1u);  // 0..NB-1, larger units higher
+        q = q > NB - 1 ? NB - 1 : q;
+        bk[i] = NB - 1 - (uint32_t)q;  // 0: largest
+        atomicAdd(&cnt[bk[i]], e);
+    }
+    lds_sync();
+    const uint32_t x = bid % BALANCE_XCDS, k = bid / BALANCE_XCDS;
+    const uint32_t g = (k % BALANCE_CUS_PER_XCD) * BALANCE_XCDS + x;
+    const uint32_t j = k / BALANCE_CUS_PER_XCD;
+    const uint32_t rank = j * BALANCE_CUS + ((j & 1u) ? BALANCE_CUS - 1 - g : g);
+    // bucket holding the rank and the rank within it (the same in every
+    // thread): lane b scans bucket b's count
+    const uint32_t lb = lane_id();
+    const uint32_t cb = lb < (uint32_t)NB ? cnt[lb] : 0u;
+    const uint32_t incl = wave_scan(cb, 0u, OpAdd());
+    const uint64_t past = ballot(lb < (uint32_t)NB && incl > rank);
+    if (past == 0) {  // (uniform) past the last unit
+        lds_sync();   // every thread has read the counts
+        c = -1;
+        eff = 1;
+        base = 0;
+        n = 0;
+        ubase = 0;
+        return 0;
+    }
+    const uint32_t want = (uint32_t)__builtin_ctzll(past);
+    const uint32_t m = rank - (uint32_t)__builtin_amdgcn_readlane((int)(incl - cb), (int)want);
+    // Rows in row order (row i * NT + t is thread t's chunk i): wave prefix
+    // sums of their unit counts, in the wanted bucket and over every row.
+    const uint32_t w = threadIdx.x >> 6;
+    uint32_t exw[MAXPER], exa[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        const uint32_t vw = bk[i] == want ? we[i] : 0u;
+        const uint32_t iw = wave_scan(vw, 0u, OpAdd());
+        const uint32_t ia = wave_scan(we[i], 0u, OpAdd());
+        exw[i] = iw - vw;
+        exa[i] = ia - we[i];
+        if (lane_id() == 63) {
+            wcnt[i * WAVES + w] = iw;
+            wall[i * WAVES + w] = ia;
+        }
+    }
+    lds_sync();
+    uint32_t before = 0, beforea = 0;  // units before chunk i: wanted bucket / every row
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        uint32_t mine = 0, chunk = 0, minea = 0, chunka = 0;
+#pragma unroll
+        for (int v = 0; v < WAVES; ++v) {
+            const uint32_t cw = wcnt[i * WAVES + v], ca = wall[i * WAVES + v];
+            mine += (uint32_t)v < w ? cw : 0u;
+            chunk += cw;
+            minea += (uint32_t)v < w ? ca : 0u;
+            chunka += ca;
+        }
+        const uint32_t r0 = before + mine + exw[i];
+        if (bk[i] == want && m >= r0 && m < r0 + we[i]) {
+            found[0] = threadIdx.x + (uint32_t)i * NT;
+            found[1] = wb[i];
+            found[2] = wn[i];
+            found[3] = m - r0;
+            found[4] = we[i];
+            found[5] = beforea + minea + exa[i];
+        }
+        before += chunk;
+        beforea += chunka;
+    }
+    lds_sync();
+    const int row = (int)found[0];
+    base = found[1];
+    n = found[2];
+    c = (int)found[3];
+    eff = (int)found[4];
+    ubase = found[5];
+    lds_sync();  // the histogram is rewritten later
+    if (row >= 0 && row < p.num_rows) return row;
+    c = -1;  // not reached: every rank below the unit count names a unit
+    return 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -2043,10 +2153,15 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     // no per-lane loop.
     int64_t base, n;
     int r, c = 0, beff = 1;
+    uint32_t ubase = 0;  // (units) the row's first unit
     if (p.balance) {
-        r = balanced_row<Policy>(sm, p, bid, base, n, c, beff);
+        if (p.helpers)
+            r = placed_unit<Policy>(sm, p, bid, base, n, c, beff, ubase);
+        else
+            r = balanced_row<Policy>(sm, p, bid, base, n, c, beff);
         c = __builtin_amdgcn_readfirstlane(c);
-        if (c < 0) return;  // a helper slot without a row
+        if (c < 0) return;  // a workgroup past the last unit
+        ubase = (uint32_t)__builtin_amdgcn_readfirstlane((int)ubase);
     } else {
         r = (int)(unit / (uint32_t)p.nsplit);
         Policy::window(p, r, base, n);
@@ -2082,10 +2197,11 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     if (eff64 < 1) eff64 = 1;
     const int eff = p.balance ? __builtin_amdgcn_readfirstlane(beff) : (int)eff64;
     if (c >= eff) return;
-    // a placed row that may be split has units r * nsplit + c, as elsewhere
-    // (the split-row merge finds the lists and counts there); other placed
-    // rows keep their workgroup's own unit
-    if (p.helpers) unit = (uint32_t)r * (uint32_t)p.nsplit + (uint32_t)c;
+    // The row's units, which the split-row merge reads: ubase + c with the
+    // length-balanced units, r * nsplit + c otherwise (a placed row of whole
+    // units keeps its workgroup's own unit).
+    const uint32_t unit0 = p.helpers ? ubase : (uint32_t)r * (uint32_t)p.nsplit;
+    if (p.helpers) unit = ubase + (uint32_t)c;
 
     const Slice s = make_slice<DT>(row, n, c, eff);
     uint32_t* gkey = p.ws_key + (size_t)unit * (uint32_t)p.ws_slots;
@@ -2247,7 +2363,6 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
         __syncthreads();
         VTS_STAMP(5);
         if (sm.flag == 0) return;
-        const uint32_t unit0 = (uint32_t)r * (uint32_t)p.nsplit;
         if (threadIdx.x < (unsigned)eff) {
             sm.seg_hi[threadIdx.x] = gload(p.ws_count + unit0 + threadIdx.x);
             sm.seg_lo[threadIdx.x] = gload(p.ws_count_up + unit0 + threadIdx.x);
@@ -2355,7 +2470,6 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     if (sm.flag == 0) return;
 
     // last unit of the row: merge
-    const uint32_t unit0 = (uint32_t)r * (uint32_t)p.nsplit;
     const uint32_t* rkey = p.ws_key + (size_t)unit0 * (uint32_t)p.ws_slots;
     const uint32_t* ridx = p.ws_idx + (size_t)unit0 * (uint32_t)p.ws_slots;
     // With at most GL lists, the first GL_SLOTS entries of every list (of
