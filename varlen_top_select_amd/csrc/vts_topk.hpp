@@ -2480,6 +2480,7 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
     // 32-bit keys only: measured on the 16-bit kernels (two lists per split
     // row there), the read-ahead cost more than the round trip it saves.
     constexpr int GL = 4, GPL = 4, GS = GL * GPL;
+    constexpr int GLB = 8;  // lists whose bounds the gather below keeps in registers
     constexpr uint32_t GL_SLOTS = (uint32_t)(GPL * NT);
     static_assert(GL_SLOTS <= (uint32_t)HI_SLOTS, "read-ahead within a unit's workspace slots");
     const bool ahead = Traits<DT>::BITS > 16 && eff <= GL && (uint32_t)p.ws_slots >= own + GL_SLOTS;
@@ -2552,6 +2553,49 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
                 if (q < eff && j < gcount[q]) {
                     sm.key[gbase[q] + j] = gk[e];
                     sm.idx[gbase[q] + j] = gi[e];
+                }
+            }
+            __syncthreads();
+            select_and_emit<DT, Policy>(sm, p, r, base, row, LdsSrc<ONCHIP_J>(sm, th, rupper ? G.T2 : 0u));
+            VTS_STAMP(4);
+            return;
+        }
+        if (!ORD && !ahead && eff <= GLB) {  // (lists not read ahead; ORD: registers)
+            // At most GLB lists: gathered entry i of list q (lists in order,
+            // entry i at or past its first gathered slot gb[q]) is workspace
+            // entry i + dl[q] from the row's first list; the list of each
+            // entry is found by comparisons with the bounds, which every lane
+            // holds (no loop over LDS), eight entries per thread per round
+            // with all their loads in flight.
+            uint32_t gb[GLB], dl[GLB];
+            uint32_t acc = 0;
+#pragma unroll
+            for (int q = 0; q < GLB; ++q) {
+                const uint32_t from = q == c ? own : 0u;
+                gb[q] = q < eff ? acc : 0xFFFFFFFFu;
+                dl[q] = (uint32_t)q * (uint32_t)p.ws_slots + from - acc;  // (mod 2^32)
+                if (q < eff) acc += sm.seg_hi[q] - from;
+            }
+            constexpr int E = 8;
+            for (uint32_t b0 = 0; b0 < m; b0 += (uint32_t)NT * E) {
+                uint32_t kk[E], cc[E];
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint32_t i = b0 + (uint32_t)e * NT + threadIdx.x;
+                    uint32_t d = dl[0];
+#pragma unroll
+                    for (int q = 1; q < GLB; ++q) d = i >= gb[q] ? dl[q] : d;
+                    const uint32_t at = i < m ? i + d : 0u;  // < (unit's lists) * ws_slots
+                    kk[e] = gload(rkey + at);
+                    cc[e] = gload(ridx + at);
+                }
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const uint32_t i = b0 + (uint32_t)e * NT + threadIdx.x;
+                    if (i < m) {
+                        sm.key[own + i] = kk[e];
+                        sm.idx[own + i] = cc[e];
+                    }
                 }
             }
             __syncthreads();
