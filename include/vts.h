@@ -372,7 +372,9 @@ int vts_workspace_stats(void* workspace, uint32_t* out, int32_t count, void* str
  *   VTS_TUNE_LIKELY_SIGMA margin of the likely rung, same unit (0 = 20; a
  *                         value >= the safe margin merges the two rungs)
  *   VTS_TUNE_MIN_CHUNK    valid columns per workgroup below which a row is not
- *                         split further (0 = default 32768; 256..2^20)
+ *                         split further (0 = default: 32768, and 128 KB of
+ *                         columns for the length-balanced units of 512-row
+ *                         batches; 256..2^20)
  *   VTS_TUNE_NO_BALANCE   1 turns off the length-balanced placement of rows on
  *                         compute units (0 = on where it applies)
  *   VTS_TUNE_HINT_RUNG    1: vts_topk_varlen calls with a pre_idx and top_k

@@ -1,6 +1,6 @@
 """GPU parity of the length-balanced units of 512-row batches: the launch has
 1024 workgroups, and every row is cut into e = min(8, ceil(n / U)) units,
-where U is about the batch's columns per compute unit and at least 96 KB.
+where U is about the batch's columns per compute unit and at least 128 KB.
 
 Three length profiles: "few" -- a handful of long rows (e up to 8) among
 short ones, with lengths one element around a unit bound; "many" -- 200 long
@@ -27,7 +27,7 @@ W = 196608  # 768 KB of fp32, 384 KB of 16-bit columns
 
 
 def _split_cols(dtype):
-    return (96 * 1024) // (4 if dtype == F32 else 2)
+    return (128 * 1024) // (4 if dtype == F32 else 2)
 
 
 def _lengths(profile, dtype, rng):
@@ -62,7 +62,7 @@ def _varlen(profile, dtype, k, seed):
 
 def _expected_units(wl):
     """(split rows, most units of a row, units in all) under the placement's
-    rule: U = max(96 KB, min(width, 4 * sum(n >> 10) + 4 * R)) columns."""
+    rule: U = max(128 KB, min(width, 4 * sum(n >> 10) + 4 * R)) columns."""
     n = np.minimum(wl.seq_lens.astype(np.int64), W)
     U = max(_split_cols(wl.dtype), min(W, 4 * int((n >> 10).sum()) + 4 * R))
     e = np.clip(-(-n // U), 1, 8)

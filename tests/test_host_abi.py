@@ -160,19 +160,19 @@ def test_transform_argument_errors(lib, kw, want):
 
 
 def test_workspace_second_workgroups(lib):
-    """512 rows whose windows can hold 96 KB get two units per row in the
+    """512 rows whose windows can hold 128 KB get two units per row in the
     workspace (the length-balanced placement cuts long rows into units of at
-    least 96 KB, at most 1024 units in all); narrower rows, other row counts
+    least 128 KB, at most 1024 units in all); narrower rows, other row counts
     and the placement switched off keep one."""
     vb = lib.vts_topk_varlen_workspace_bytes
-    two = vb(512, 49152, 1024, 1)      # bf16: 49152 columns are 96 KB
-    narrow = vb(512, 49151, 1024, 1)
+    two = vb(512, 65536, 1024, 1)      # bf16: 65536 columns are 128 KB
+    narrow = vb(512, 65535, 1024, 1)
     assert two > narrow
-    assert vb(512, 24576, 1024, 0) > vb(512, 24575, 1024, 0)  # fp32: 24576 columns
+    assert vb(512, 32768, 1024, 0) > vb(512, 32767, 1024, 0)  # fp32: 32768 columns
     assert vb(768, 262144, 1024, 1) == vb(768, 1024, 1024, 1)  # 768 rows: one unit each
     assert lib.vts_set_tuning(vts.TUNE_NO_BALANCE, 1) == OK
     try:
-        assert vb(512, 49152, 1024, 1) < two
+        assert vb(512, 65536, 1024, 1) < two
     finally:
         assert lib.vts_set_tuning(vts.TUNE_NO_BALANCE, 0) == OK
 

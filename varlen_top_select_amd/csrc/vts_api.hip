@@ -56,10 +56,11 @@ size_t itemsize(int32_t dtype) { return dtype == VTS_F32 ? 4 : 2; }
 // kernel): one workgroup's stream is capped by the memory requests its
 // compute unit keeps in flight (~20 GB/s), so a row far longer than the mean
 // would otherwise finish long after the rest.  A unit is at least
-// MIN_UNIT_BYTES long: a split pays a sample per unit and a merge.  The rows
+// MIN_UNIT_BYTES long: a split pays a sample per unit and a merge (DSv4 MTP,
+// cold: 29.0 us at 128 KB, 30.8 at 96, 29.9 at 192, 31.9 at 64).  The rows
 // are known only on the device, which decides per row; the plan reserves the
 // workgroups and the workspace.
-constexpr int64_t MIN_UNIT_BYTES = 96 * 1024;
+constexpr int64_t MIN_UNIT_BYTES = 128 * 1024;
 
 int32_t split_cols(int32_t dtype) { return (int32_t)(MIN_UNIT_BYTES / (int64_t)itemsize(dtype)); }
 
@@ -205,7 +206,7 @@ void fill_plan(Params& p, int64_t num_rows, int64_t width, void* ws, int32_t slo
     // length-balanced row placement: one workgroup per row, whole slots on all
     // 256 CUs (2..4 rows per CU, all resident at once)
     p.helpers = helpers && placed ? 1 : 0;
-    p.split_cols = split_cols(dtype);
+    p.split_cols = g_tune.min_chunk > 0 ? g_tune.min_chunk : split_cols(dtype);
     p.balance = ((ns == 1 && num_rows % BALANCE_CUS == 0 && num_rows >= 2 * BALANCE_CUS &&
                   num_rows <= 4 * BALANCE_CUS && placed) || p.helpers)
                     ? 1 : 0;

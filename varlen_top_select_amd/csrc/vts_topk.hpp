@@ -56,7 +56,7 @@
 // stamps the start of its publication (11) and the barrier after it (12),
 // and its merging unit the moment it has read the lists' counts (10); the
 // emission stamps its output tickets (13) and, with a page table, the staged
-// table (14).
+// table (14); the sample stamps its arrival (15).
 #ifdef VTS_PHASE_STAMPS
 #define VTS_STAMP(i)                                                           \
     do {                                                                       \
@@ -2267,7 +2267,10 @@ __device__ __forceinline__ void topk_unit(Smem& sm, const Params& p, uint32_t bi
                 lds_sync();
             }
         }
-        G = sample_rungs<DT>(sm, p, n, S, [&]() { load_step(RA, rs, order.first(0, STEP)); });
+        G = sample_rungs<DT>(sm, p, n, S, [&]() {
+            VTS_STAMP(15);
+            load_step(RA, rs, order.first(0, STEP));
+        });
         if constexpr (HINT) {  // both rungs are lower bounds of the k-th largest key
             G.T = G.T > TH ? G.T : TH;
             G.T2 = G.T2 > TH ? G.T2 : TH;

@@ -63,12 +63,14 @@ def report(name: str, st: np.ndarray, event_us: float) -> None:
     st = st[st[:, 0] > 0]
     t0 = st[:, 0].min()
     us = lambda i: np.where(st[:, i] > 0, (st[:, i] - t0) / 100.0, np.nan)  # 100 MHz ticks
-    s = {i: us(i) for i in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 14)}
+    s = {i: us(i) for i in (0, 1, 2, 3, 4, 5, 8, 9, 10, 11, 12, 13, 14, 15)}
     n = (st[:, 7] >> 32).astype(np.int64)
     print(f"== {name}: {st.shape[0]} units, kernel time by events {event_us:.1f} us")
     print("  unit start            ", _pct(s[0]))
     print("  window known          ", _pct(s[1]))
     print("  window -> rungs       ", _pct(s[2] - s[1]))
+    print("    window -> sample in ", _pct(s[15] - s[1]))
+    print("    sample in -> rungs  ", _pct(s[2] - s[15]))
     print("  rungs -> stream end   ", _pct(s[3] - s[2]))
     print("  stream end -> written ", _pct(s[4] - s[3]))
     print("    stream end -> select", _pct(s[8] - s[3]))
