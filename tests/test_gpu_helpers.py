@@ -127,3 +127,23 @@ def test_helpers_page_transform():
     out, raw, _ = run_transform(wl)
     errs = check_transform_wl(wl, out, raw)
     assert errs == [], "\n".join(errs[:8])
+
+
+def test_helpers_unit_cap():
+    """Rows longer than 8 U: the unit count stops at 8 and each unit is longer
+    than U (fp32, four rows of 300000 columns among short rows)."""
+    Wc = 300000
+    rng = np.random.default_rng(903)
+    n = rng.integers(100, 3001, size=R).astype(np.int64)
+    at = rng.choice(R, size=4, replace=False)
+    n[at] = Wc - rng.integers(0, 8, size=4)
+    x = rng.standard_normal((R, Wc), dtype=np.float32).view(np.uint32)
+    wl = Workload(name="helpers-cap", kind="varlen", dtype=F32, x=x, width=Wc, k=2048,
+                  seq_lens=n.astype(np.int32), next_n=1, compress_ratio=1, pre_idx=None,
+                  return_values=True)
+    U = max(_split_cols(F32), min(Wc, 4 * int((np.minimum(n, Wc) >> 10).sum()) + 4 * R))
+    assert -(-int(n.max()) // U) > 8, "the long rows need more than eight units"
+    say(f"units varlen capped at 8 units: 4 rows of ~{Wc} fp32 columns, U = {U}")
+    idx, vals, _ = run_varlen(wl)
+    errs = check_varlen(wl, idx, vals)
+    assert errs == [], "\n".join(errs[:8])
