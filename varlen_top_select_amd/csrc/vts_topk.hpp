@@ -835,15 +835,16 @@ __device__ __forceinline__ int32_t vec_max_raw(const u32x4& q) {
     }
 }
 
-// Drains slots [0, sc) of a wave's staging queue (sc <= 64, wave-uniform) in
-// one round: lane l takes slot l and runs the element filter on its vector;
+// Drains the first sc entries of a wave's staging queue (sc <= 64,
+// wave-uniform), which start at slot `head` of the wave's ring, in one round:
+// lane l takes entry l and runs the element filter on its vector;
 // the candidates get one LDS ticket as in filter_step and the keys >= T2 are
 // added to `upc`.  Every lane of the wave calls it; no barrier (the queue is
 // the wave's own).
 template <int DT, bool CANON>
 __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col0,
                                             const RungTest<DT, true, CANON>& test, uint32_t sc,
-                                            uint32_t& upc) {
+                                            uint32_t head, uint32_t& upc) {
     constexpr int VE = Traits<DT>::VE;
     constexpr uint32_t F = fail_word<DT>();
     const uint32_t base = (threadIdx.x >> 6) * STAGE;
@@ -851,8 +852,9 @@ __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col
     u32x4 q = u32x4{F, F, F, F};
     uint32_t v = 0;
     if (l < sc) {
-        q = sm.stage.vec[base + l];
-        v = sm.stage.v[base + l];
+        const uint32_t slot = base + ((head + l) & (STAGE - 1));
+        q = sm.stage.vec[slot];
+        v = sm.stage.v[slot];
     }
     uint32_t ti = 0;
 #pragma unroll
@@ -879,18 +881,22 @@ __device__ __forceinline__ void drain_stage(Smem& sm, const Buf& B, uint32_t col
 
 // One streaming step with both rungs >= +0.  Per vector: the largest raw
 // element against the safe rung T; the (few) vectors holding a candidate are
-// appended to the wave's staging queue in LDS (ballot + mbcnt positions).
-// Whenever STAGE_DRAIN are queued, a round of STAGE_DRAIN is drained and the
-// rest moves to the front, so the per-element work runs on rounds of staged
-// vectors instead of on every element of the step.
+// appended to the wave's staging queue in LDS (ballot + mbcnt positions), a
+// ring of STAGE slots whose sc entries start at slot `head`.  Whenever
+// STAGE_DRAIN are queued, a round of STAGE_DRAIN is drained from the head,
+// which then moves on by STAGE_DRAIN (so it is 0 or STAGE_DRAIN), and the
+// per-element work runs on rounds of staged vectors instead of on every
+// element of the step.
 template <int DT, bool CANON>
 __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (&R)[Traits<DT>::U],
                                            uint32_t first, uint32_t col0,
                                            const RungTest<DT, true, CANON>& test, uint32_t& sc,
-                                           uint32_t& upc) {
+                                           uint32_t& head, uint32_t& upc) {
     // Drains run while at least STAGE_DRAIN vectors are queued, so a vector's
-    // 64 writes start at sc <= STAGE_DRAIN - 1 and end inside the queue.
+    // 64 writes start at sc <= STAGE_DRAIN - 1 entries past the head and end
+    // before it comes round again: the queued entries are never overwritten.
     static_assert(STAGE_DRAIN - 1 + 64 <= STAGE && STAGE_DRAIN <= 64, "staging queue bound");
+    static_assert(STAGE == 2 * STAGE_DRAIN && (STAGE & (STAGE - 1)) == 0, "ring of two rounds");
     const uint32_t base = (threadIdx.x >> 6) * STAGE;
     const uint32_t l = lane_id();
 #pragma unroll
@@ -898,23 +904,18 @@ __device__ __forceinline__ void stage_step(Smem& sm, const Buf& B, const u32x4 (
         const bool hit = vec_max_raw<DT>(R[u]) >= test.a;
         const uint64_t m = ballot(hit);
         const uint32_t nh = (uint32_t)__popcll(m);
-        // Every lane writes, without branching: hits to slots [sc, sc + nh) in
-        // lane order, the others to [sc + nh, sc + 64), which later entries
+        // Every lane writes, without branching: hits to entries [sc, sc + nh)
+        // in lane order, the others to [sc + nh, sc + 64), which later entries
         // overwrite and the drain never reads.
         const uint32_t below = mbcnt(m);
-        const uint32_t pos = base + sc + (hit ? below : nh + (l - below));
+        const uint32_t pos = base + ((head + sc + (hit ? below : nh + (l - below))) & (STAGE - 1));
         sm.stage.vec[pos] = R[u];
         sm.stage.v[pos] = first + (uint32_t)u * NT + threadIdx.x;
         sc += nh;
-        while (sc >= (uint32_t)STAGE_DRAIN) {
-            drain_stage<DT, CANON>(sm, B, col0, test, STAGE_DRAIN, upc);
+        if (sc >= (uint32_t)STAGE_DRAIN) {  // (sc < 2 * STAGE_DRAIN: one round at most)
+            drain_stage<DT, CANON>(sm, B, col0, test, STAGE_DRAIN, head, upc);
             sc -= STAGE_DRAIN;
-            if (l < sc) {  // the rest to the front (the wave's own slots, in order)
-                const u32x4 q = sm.stage.vec[base + STAGE_DRAIN + l];
-                const uint32_t v = sm.stage.v[base + STAGE_DRAIN + l];
-                sm.stage.vec[base + l] = q;
-                sm.stage.v[base + l] = v;
-            }
+            head ^= (uint32_t)STAGE_DRAIN;
         }
     }
 }
@@ -956,12 +957,13 @@ __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[
                                             uint32_t col0, const Rungs& G, const StepOrder& order) {
     constexpr uint32_t STEP = (uint32_t)NT * Traits<DT>::U;
     const RungTest<DT, FAST, CANON> test(G);
-    uint32_t sc = 0;   // staged vectors of this wave (FAST)
-    uint32_t upc = 0;  // keys >= T2 seen by this wave
+    uint32_t sc = 0;    // staged vectors of this wave (FAST)
+    uint32_t head = 0;  // first staged slot of the wave's ring (FAST)
+    uint32_t upc = 0;   // keys >= T2 seen by this wave
     auto step = [&](u32x4 (&R)[Traits<DT>::U], uint32_t vs) {
         if constexpr (FAST) {
             if (vs + STEP > nvec) pad_step<DT>(R, vs, nvec);
-            stage_step<DT, CANON>(sm, B, R, vs, col0, test, sc, upc);
+            stage_step<DT, CANON>(sm, B, R, vs, col0, test, sc, head, upc);
         } else {
             filter_step<DT, false, CANON>(sm, B, R, vs, nvec, col0, test, upc);
         }
@@ -983,7 +985,7 @@ __device__ __forceinline__ void stream_unit(Smem& sm, const Buf& B, u32x4 (&RA)[
         step(RA, order.first(s + 1, STEP));
     }
     if constexpr (FAST) {
-        if (sc) drain_stage<DT, CANON>(sm, B, col0, test, sc, upc);
+        if (sc) drain_stage<DT, CANON>(sm, B, col0, test, sc, head, upc);
     }
     if (lane_id() == 0 && upc) atomicAdd(&sm.up_n, upc);
 }
