@@ -353,13 +353,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t body_rsrc(const void* base, ui
                                              0x00020000);
 }
 
-// Cache policy of the row's streaming loads (the sample and the stream): the
-// non-temporal hint (gfx950 cache-policy bit NT).  Every byte of a row is read
-// once, and with the hint a plain 16-byte streaming read of 820 MB measured
-// 6.82-6.93 TB/s on MI355X against 6.01-6.13 without it (sc0 or sc1 alone: no
-// gain).  The workspace lists, which the merge and the wide selections read
-// more than once, keep the default policy.
+// Cache policy of the stream's loads: the non-temporal hint (gfx950
+// cache-policy bit NT).  Every byte of the stream is read once, and with the
+// hint a plain 16-byte streaming read of 820 MB measured 6.82-6.93 TB/s on
+// MI355X against 6.01-6.13 without it (sc0 or sc1 alone: no gain).  The
+// sample, whose blocks the stream reads again later, and the workspace lists,
+// which the merge and the wide selections read more than once, keep the
+// default policy (the sample with the hint as well: the 1024 x 262144 fp32
+// batch 143.7-145.1 us warm, 146.7-147.5 cold, against 142.0-143.7 and
+// 142.0-144.2 without it).
 constexpr int LOAD_NT = 2;
+constexpr int LOAD_SAMPLE = 0;
 
 // Loads one streaming step: vector first + u*NT + threadIdx.x into R[u]
 // (zeros past the end).
@@ -482,7 +486,7 @@ __device__ __forceinline__ void sample_load(const typename Traits<DT>::raw_t* ro
         const uint32_t gl = g0 + ((lead - g0) & 7u);   // ... on a 128-byte line
         const uint32_t gv = whole ? g : gl + g % VPB;
         S.v[j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(gv * 16u), 0, LOAD_NT));
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(gv * 16u), 0, LOAD_SAMPLE));
 #pragma unroll
         for (uint32_t e = 0; e < VE; ++e) {
             const int64_t col = (int64_t)(gv * VE + e) - (int64_t)mis;
