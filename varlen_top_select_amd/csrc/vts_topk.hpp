@@ -359,9 +359,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t body_rsrc(const void* base, ui
 // MI355X against 6.01-6.13 without it (sc0 or sc1 alone: no gain).  The
 // sample, whose blocks the stream reads again later, and the workspace lists,
 // which the merge and the wide selections read more than once, keep the
-// default policy (the sample with the hint as well: the 1024 x 262144 fp32
-// batch 143.7-145.1 us warm, 146.7-147.5 cold, against 142.0-143.7 and
-// 142.0-144.2 without it).
+// default policy.  (Measured on the 1024 x 262144 fp32 batch, one box: with
+// the hint on the sample as well, 143.7-145.1 us warm and 146.7-147.5 cold;
+// with the sample on the default policy, 142.0-143.7 and 142.0-144.2.)
 constexpr int LOAD_NT = 2;
 constexpr int LOAD_SAMPLE = 0;
 
