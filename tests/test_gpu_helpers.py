@@ -129,6 +129,19 @@ def test_helpers_page_transform():
     assert errs == [], "\n".join(errs[:8])
 
 
+@pytest.mark.parametrize("seed", [904, 905, 906])
+def test_helpers_spread_seeds(seed):
+    """More log-uniform length draws (fp32 and bf16 alternately): every unit
+    count from 1 to the maximum, at other positions."""
+    dtype = F32 if seed % 2 == 0 else BF16
+    wl = _varlen("spread", dtype, 2048, seed)
+    split, most, units = _expected_units(wl)
+    say(f"units varlen spread seed {seed} dtype {dtype}: {split} rows split, up to {most} units")
+    idx, vals, _ = run_varlen(wl)
+    errs = check_varlen(wl, idx, vals)
+    assert errs == [], "\n".join(errs[:8])
+
+
 def test_helpers_unit_cap():
     """Rows longer than 8 U: the unit count stops at 8 and each unit is longer
     than U (fp32, four rows of 300000 columns among short rows)."""

@@ -49,7 +49,7 @@ def _row(rng, size, distinct, above):
     return row
 
 
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2, 3])
 def test_select_range_clusters(seed):
     rng = np.random.default_rng(9100 + seed)
     x = np.stack([_row(rng, *spec) for spec in ROWS]).view(np.uint32)
